@@ -1,0 +1,161 @@
+/*
+ * sparse_attn.h: C ABI of the MI355X (gfx950) top-k sparse attention library.
+ *
+ * The library computes two forms of the same attention:
+ *   1. sparse_attn_fwd: each query token attends to K rows of a shared
+ *      key/value cache picked by an index list (-1 = empty slot), with a
+ *      per-head "sink" logit that takes part in the softmax normalisation only.
+ *   2. topk_bitmask_build + masked_attn_fwd: the index lists scattered into a
+ *      bit-packed mask, consumed by a dense attention that reads the mask
+ *      words 4 at a time (one 16-byte load per 128 keys).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device memory on the current device;
+ *    "host" pointers are ordinary CPU memory. bf16 data is passed as raw
+ *    16-bit storage (the high half of an IEEE single). Every tensor is dense
+ *    and row-major in the layout stated; the caller owns every buffer.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    on it; no entry point synchronises, allocates device memory or keeps
+ *    state between calls.
+ *  - All arguments are checked on the host before any HIP call; a rejected
+ *    call returns a nonzero sa_status and touches no memory. Launch failures
+ *    return SA_ERR_HIP; faults inside a kernel surface at the caller's next
+ *    synchronisation.
+ *  - Zero-sized work returns SA_OK without launching anything.
+ *  - Outputs must not alias inputs.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SA_ERR_SHAPE = 2,       /* a size is negative or sizes are inconsistent */
+  SA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  SA_ERR_UNSUPPORTED = 4, /* a head dimension / head count this build has no kernel for */
+  SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  SA_ERR_HIP = 6          /* a HIP call (launch) failed */
+} sa_status;
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* sa_status_string(int status);
+
+/* ------------------------------------------------------------------------ */
+/* Top-k sparse attention.                                                   */
+/* Operation ("DeepSeek V4 源码剖析", ch. 5, sections 5.1-5.2, 5.4-5.5):     */
+/*   for every batch b, token s, head h, with V = { k : 0 <= idx[b,s,k] < T }  */
+/*   (duplicates counted; -1 or any index outside [0, T) is an empty slot):    */
+/*     x_k  = scale * dot(q[b,s,h,:], kv[b, idx[b,s,k], :])                    */
+/*     w    = softmax over { x_k : k in V } plus one extra logit sink[h]       */
+/*     o[b,s,h,:] = sum_{k in V} w_k * kv[b, idx[b,s,k], :]   (sink has no row) */
+/*   The same kv row serves as key and value (one shared row for all heads).   */
+/*   sink[h] = +inf gives o = 0; -inf means no sink; NaN gives a NaN row;      */
+/*   no valid slot and sink -inf gives o = 0.                                  */
+/*   Arithmetic: bf16 products, fp32 accumulation, fp32 softmax; the softmax   */
+/*   weights are rounded to bf16 before the weighted row sum; o is rounded to  */
+/*   bf16 (nearest even).                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Bytes of device workspace sparse_attn_fwd needs for this shape and split
+ * count (num_splits = 0 picks the library's choice, as sparse_attn_fwd does).
+ * Returns 0 when no workspace is needed, and also for invalid sizes.
+ */
+size_t sparse_attn_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K, int num_splits);
+
+/*
+ * The split count sparse_attn_fwd uses for num_splits = 0 (each token's K
+ * slots are cut into this many contiguous ranges processed by separate
+ * workgroups and merged afterwards). Returns 1 for invalid sizes.
+ */
+int sparse_attn_num_splits(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K);
+
+/*
+ * q          device, bf16 [B][S][H][D]
+ * kv         device, bf16 [B][T][D]
+ * attn_sink  device, fp32 [H]
+ * topk_idxs  device, int32 [B][S][K]
+ * out        device, bf16 [B][S][H][D] (written in full)
+ * scale      the softmax scale (the pages use D^-0.5)
+ * num_splits 0 = library choice, else 1..64 (clamped to K's tile count)
+ * workspace  device, >= sparse_attn_workspace_bytes(...) bytes, 256-byte
+ *            aligned; may be NULL when that size is 0. Contents on entry do
+ *            not matter; contents on return are unspecified.
+ * Supported: D in {64, 512}; 1 <= H <= 128. q, kv, out 16-byte aligned.
+ */
+int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                    int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Bit-packed top-k mask.                                                    */
+/* Shape rule and row layout: prhub summary of vLLM PR #52217, key source    */
+/* (_topk_mask_shape, _build_topk_mask) and its tests; bit order: prhub      */
+/* summary of vLLM PR #48770, key source (dense_mask_mod: word j >> 5,       */
+/* bit j & 31, least significant bit first).                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Host-only. Writes {B, padded_q, words} to out_shape (host, 3 entries):
+ *   padded_q = max_q_len rounded up to 128 when max_q_len <= 128, else to 256;
+ *   words    = ceil(max_key_len / 32) + (reserve_key_start_word ? 1 : 0),
+ *              rounded up to a multiple of 4 (rows are whole 16-byte chunks).
+ */
+int topk_bitmask_shape(int64_t B, int64_t max_q_len, int64_t max_key_len, int reserve_key_start_word,
+                       int64_t* out_shape);
+
+/*
+ * topk_idxs  device, int32 [B][Q][topk]
+ * q_lens     device, int32 [B] or NULL (NULL: all Q rows of every batch are live)
+ * key_starts device, int32 [B] or NULL; when given, words must hold the reserved
+ *            word: words >= ceil(key_len / 32) + 1
+ * mask       device, uint32 [B][padded_q][words], written in FULL (no pre-zeroing):
+ *              bit (j & 31) of mask[b][q][j >> 5] is set iff q < q_len[b] and
+ *              some slot of topk_idxs[b][q] equals j with 0 <= j < key_len;
+ *              mask[b][0][words-1] = key_starts[b] when key_starts is given;
+ *              every other word is 0.
+ * Requires padded_q >= Q, words % 4 == 0, 32 * words >= key_len, mask 16-byte aligned.
+ */
+int topk_bitmask_build(const int32_t* topk_idxs, const int32_t* q_lens, const int32_t* key_starts, uint32_t* mask,
+                       int64_t B, int64_t Q, int64_t topk, int64_t key_len, int64_t padded_q, int64_t words,
+                       void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Masked dense attention (the masked-MHA form).                             */
+/* prhub summary of vLLM PR #48770 (masked MHA emulating sparse attention    */
+/* for short prefills; dense_mask_mod) and of vLLM PR #52217 (mask words     */
+/* loaded 4 at a time, bitwise-identical results).                           */
+/*   for b, query q, head h, with J = { j < KV : mask == NULL or bit j of     */
+/*   mask[b][q] is set } (one mask row shared by all heads, no sink):         */
+/*     o[b,q,h,:] = sum_{j in J} softmax_j(scale * q[b,q,h,:].k[b,j,h,:]) v[b,j,h,:] */
+/*   J empty gives o = 0.                                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * q     device, bf16 [B][Q][H][Dqk]
+ * k     device, bf16 [B][KV][H][Dqk]
+ * v     device, bf16 [B][KV][H][Dv]
+ * mask  device, uint32 [B][padded_q][words] or NULL (NULL: every key visible)
+ * out   device, bf16 [B][Q][H][Dv] (written in full)
+ * mask_load_bits  128: the mask is read as aligned 16-byte chunks (4 words per
+ *                 128 keys); 32: one 32-bit word per 32 keys (control variant).
+ *                 Both give bitwise-identical outputs.
+ * Supported: (Dqk, Dv) = (192, 128). Requires padded_q >= Q, words % 4 == 0,
+ * 32 * words >= KV; q, k, v, mask, out 16-byte aligned.
+ */
+int masked_attn_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
+                    int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
+                    int64_t words, float scale, int mask_load_bits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */
