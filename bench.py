@@ -1,0 +1,235 @@
+"""Throughput of top-k sparse attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|prefill|ragged|masked|bitmask]
+
+One step is one pass of the hot path over one batch of synthetic input that is
+already resident in HBM. The default workload is the decode shape B=64, S=1,
+H=128, D=512, K=1152 (128 window + 1024 selected slots, ~5% empty) over a
+kv cache of 128 + 8192 rows. Steps cycle through 8 independent input sets
+(~4.4 GB in total), so no step finds its rows left in the 256 MB Infinity Cache
+by an earlier step. The timed region is bracketed by device synchronisations
+and measured with HIP events recorded on the stream the kernels run on.
+
+Prints one JSON line: the metric, throughput, milliseconds per step, the
+roofline fraction of the whole call (algorithmic bytes counted from the actual
+index lists, over MI355X's 8 TB/s HBM peak) and the CPU oracle timed on the
+host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "sparse-attn query-tokens/s + % roofline (B=64,H=128,D=512,K=1152 decode)"
+NSETS = 8
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="decode", choices=["decode", "prefill", "ragged", "masked", "bitmask", "tiny"])
+    p.add_argument("--sets", type=int, default=NSETS)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def sparse_work(inp) -> tuple[float, float]:
+    """Algorithmic bytes and flops of one sparse_attn call: gathered valid rows, q, o, indices."""
+    q, idx = inp["q"], inp["topk_idxs"]
+    B, S, H, D = q.shape
+    T = inp["kv"].shape[1]
+    n_valid = int(((idx >= 0) & (idx < T)).sum().item())
+    nbytes = n_valid * D * 2 + 2 * B * S * H * D * 2 + idx.numel() * 4
+    flops = 4.0 * H * D * n_valid
+    return float(nbytes), flops
+
+
+def masked_work(inp, mask_bytes: int) -> tuple[float, float]:
+    c = inp["config"]
+    nbytes = (c.B * c.Q * c.H * c.Dqk + c.B * c.KV * c.H * (c.Dqk + c.Dv) + c.B * c.Q * c.H * c.Dv) * 2 + mask_bytes
+    flops = 2.0 * c.B * c.H * c.Q * c.KV * (c.Dqk + c.Dv)
+    return float(nbytes), flops
+
+
+def cpu_baseline(args, make_call_inputs, unit_per_call: float, unit: str, sample_desc: str):
+    """Time the CPU oracle (as it stands) on the host cores for a bounded sample."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import oracle
+
+    orc = oracle.Oracle()
+    fn, units = make_call_inputs(orc)
+    fn()  # first call outside the clock (page-in)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or el > 30.0:
+            break
+    return {"value": units * n / el, "unit": unit, "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{sample_desc}, repeated {n} times in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import top_sparse_attention_attn_amd as sa
+    from top_sparse_attention_attn_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.config in ("decode", "prefill", "ragged", "tiny"):
+        cfg = wl.SPARSE_CONFIGS[args.config]
+        nsets = args.sets if args.config != "ragged" else 1  # one ragged set is 8.6 GB of kv
+        sets = [wl.sparse_inputs(cfg, 2001 + i, dev) for i in range(nsets)]
+        out = torch.empty_like(sets[0]["q"])
+        ws_bytes = sa.sparse_attn_workspace_bytes(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)
+        ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+        ws = ws[(-ws.data_ptr()) % 256:]
+
+        def step(i):
+            x = sets[i % nsets]
+            sa.sparse_attn(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
+
+        work = [sparse_work(x) for x in sets]
+        units_per_step = cfg.B * cfg.S
+        unit = "query-tokens/s"
+        bound = "hbm" if args.config in ("decode", "ragged", "tiny") else "mfma"
+        workload = (f"{args.config} sparse_attn B={cfg.B} S={cfg.S} H={cfg.H} D={cfg.D} T={cfg.T} K={cfg.K}, "
+                    f"{nsets} rotating input sets")
+        extra_cfg = {"B": cfg.B, "S": cfg.S, "H": cfg.H, "D": cfg.D, "T": cfg.T, "K": cfg.K,
+                     "num_splits": sa.sparse_attn_num_splits(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)}
+
+        def make_cpu(orc):
+            x = sets[0]
+            qb, kvb = oracle_bits(x["q"]), oracle_bits(x["kv"])
+            sk, ix = x["attn_sink"].cpu().numpy(), x["topk_idxs"].cpu().numpy()
+            ntok = cfg.B * cfg.S
+            toks = np.arange(ntok) if args.config != "prefill" else np.arange(0, ntok, 64)
+            return (lambda: orc.sparse_attn(qb, kvb, sk, ix, x["scale"], toks)), len(toks)
+
+        sample_desc = ("all tokens of one step" if args.config != "prefill" else "every 64th token of one step")
+    else:
+        cfg = wl.MASKED_CONFIGS["masked"]
+        nsets = min(args.sets, 4)
+        sets = [wl.masked_inputs(cfg, 2001 + i, dev) for i in range(nsets)]
+        masks = [sa.topk_bitmask_build(x["topk_idxs"], cfg.KV) for x in sets]
+        if args.config == "masked":
+            out = torch.empty((cfg.B, cfg.Q, cfg.H, cfg.Dv), dtype=torch.bfloat16, device=dev)
+
+            def step(i):
+                x = sets[i % nsets]
+                sa.masked_attn(x["q"], x["k"], x["v"], masks[i % nsets], x["scale"], out=out)
+
+            work = [masked_work(x, masks[0].numel() * 4) for x in sets]
+            units_per_step = cfg.B * cfg.Q
+            unit = "query-tokens/s"
+            bound = "mfma"
+            workload = f"masked_attn B={cfg.B} Q={cfg.Q} KV={cfg.KV} H={cfg.H} qk=192 v=128, top-k mask 25% dense"
+
+            def make_cpu(orc):
+                x = sets[0]
+                qb, kb, vb = oracle_bits(x["q"]), oracle_bits(x["k"]), oracle_bits(x["v"])
+                m = masks[0].cpu().numpy().view(np.uint32)
+                rows = np.arange(0, cfg.B * cfg.Q, 64)
+                return (lambda: orc.masked_attn(qb, kb, vb, m, x["scale"], rows)), len(rows)
+
+            sample_desc = "every 64th query row of one step"
+        else:
+            outm = torch.empty_like(masks[0])
+
+            def step(i):
+                x = sets[i % nsets]
+                sa.topk_bitmask_build(x["topk_idxs"], cfg.KV, out=outm)
+
+            work = [(float(x["topk_idxs"].numel() * 4 + masks[0].numel() * 4), 0.0) for x in sets]
+            units_per_step = cfg.B * cfg.Q
+            unit = "query-rows/s"
+            bound = "hbm"
+            workload = f"topk_bitmask_build idx [2,2048,2048] -> mask [2,2048,256]"
+
+            def make_cpu(orc):
+                ix = sets[0]["topk_idxs"].cpu().numpy()
+                return (lambda: orc.topk_mask_build(ix, cfg.KV)), cfg.B * cfg.Q
+
+            sample_desc = "one full step"
+        extra_cfg = {"B": cfg.B, "Q": cfg.Q, "KV": cfg.KV, "H": cfg.H}
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    nbytes = sum(w[0] for w in work) / len(work)
+    flops = sum(w[1] for w in work) / len(work)
+    if bound == "hbm":
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    else:
+        achieved = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
+    roof["alg_bytes_per_call"] = nbytes
+    roof["alg_flops_per_call"] = flops
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, make_cpu, 0, unit, sample_desc)
+
+    rec = {
+        "metric": METRIC if args.config == "decode" else f"{args.config}: {unit}",
+        "value": units_per_step / (ms * 1e-3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if args.config != "bitmask" else "int32",
+        "data": "synthetic",
+        "config": {"workload": workload, **extra_cfg},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def oracle_bits(t):
+    import oracle
+
+    return oracle.bf16_bits(t)
+
+
+if __name__ == "__main__":
+    main()

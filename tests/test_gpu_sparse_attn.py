@@ -1,0 +1,212 @@
+"""sparse_attn on the GPU against the CPU oracle (through the C ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import top_sparse_attention_attn_amd as sa
+from top_sparse_attention_attn_amd import workloads as wl
+from gpu_util import assert_close, sparse_reference, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(inp, **kw):
+    return sa.sparse_attn(inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"], **kw)
+
+
+def _custom(B, S, H, D, T, K, seed, holes=0.1):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, T, D, generator=g).to(torch.bfloat16)
+    sink = torch.randn(H, generator=g)
+    idx = torch.stack([torch.randperm(T, generator=g)[:K] for _ in range(B * S)]).view(B, S, K).to(torch.int32)
+    idx[torch.rand(B, S, K, generator=g) < holes] = -1
+    return {"q": q.to(DEV), "kv": kv.to(DEV), "attn_sink": sink.to(DEV), "topk_idxs": idx.to(DEV), "scale": D ** -0.5}
+
+
+def test_tiny_config(oracle_impl):
+    inp = wl.sparse_inputs("tiny", 1001, DEV)
+    out = _run(inp)
+    torch.cuda.synchronize()
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, "tiny")
+
+
+@pytest.mark.parametrize("D,H", [(64, 8), (64, 40), (512, 16), (512, 128)])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_shapes_and_splits(oracle_impl, D, H, splits):
+    # K = 200 spans several 32-row tiles and ends in a ragged tile; splits > 1 exercise the combine.
+    inp = _custom(2, 3, H, D, 300, 200, seed=7 + D + H)
+    out = _run(inp, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, f"D={D} H={H} splits={splits}")
+
+
+def test_all_invalid_is_exactly_zero():
+    inp = _custom(2, 2, 128, 512, 100, 70, seed=3)
+    inp["topk_idxs"].fill_(-1)
+    for splits in (1, 2):
+        out = _run(inp, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out).item() == 0
+
+
+def test_exact_mean_bit_exact():
+    """q = 0, sink -inf, exactly 64 valid slots over {-1,0,1} rows: o is the plain mean,
+    exactly representable in bf16; any wrong or missed row changes it."""
+    g = torch.Generator().manual_seed(11)
+    B, S, H, D, T, K = 2, 3, 128, 512, 500, 150
+    kv = torch.randint(-1, 2, (B, T, D), generator=g).to(torch.bfloat16)
+    q = torch.zeros(B, S, H, D, dtype=torch.bfloat16)
+    idx = torch.full((B, S, K), -1, dtype=torch.int32)
+    ref = torch.zeros(B, S, D, dtype=torch.float64)
+    for b in range(B):
+        for s in range(S):
+            rows = torch.randperm(T, generator=g)[:64]
+            idx[b, s, torch.randperm(K, generator=g)[:64]] = rows.to(torch.int32)
+            ref[b, s] = kv[b, rows].double().mean(0)
+    sink = torch.full((H,), float("-inf"))
+    for splits in (1, 3):
+        out = sa.sparse_attn(q.to(DEV), kv.to(DEV), sink.to(DEV), idx.to(DEV), 1.0, num_splits=splits)
+        torch.cuda.synchronize()
+        got = out.double().cpu()
+        assert torch.equal(got, ref.unsqueeze(2).expand(B, S, H, D)), f"splits={splits}"
+
+
+def test_single_row_bit_exact():
+    inp = _custom(1, 2, 128, 512, 90, 40, seed=5)
+    inp["topk_idxs"].fill_(-1)
+    inp["topk_idxs"][:, :, 17] = 33
+    inp["attn_sink"].fill_(float("-inf"))
+    for splits in (1, 2):
+        out = _run(inp, num_splits=splits)
+        torch.cuda.synchronize()
+        row = inp["kv"][0, 33]
+        assert torch.equal(out[0], row.expand_as(out[0]))
+
+
+def test_sink_special_values(oracle_impl):
+    inp = _custom(1, 2, 16, 64, 90, 40, seed=6)
+    inp["attn_sink"][0] = float("inf")
+    inp["attn_sink"][1] = float("nan")
+    inp["attn_sink"][2] = float("-inf")
+    inp["attn_sink"][3] = 100.0
+    for splits in (1, 2):
+        out = _run(inp, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out[:, :, 0]).item() == 0
+        assert torch.isnan(out[:, :, 1]).all()
+        ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+        assert_close(to64(out).reshape(ref.shape), ref, f"sink specials splits={splits}")
+
+
+def test_sink_halves_mean():
+    """q = 0 and sink = ln(n): o is half the mean of the n rows."""
+    g = torch.Generator().manual_seed(8)
+    T, D, n = 300, 512, 100
+    kv = torch.randn(1, T, D, generator=g).to(torch.bfloat16)
+    q = torch.zeros(1, 1, 128, D, dtype=torch.bfloat16)
+    idx = torch.randperm(T, generator=g)[:n].view(1, 1, n).to(torch.int32)
+    sink = torch.full((128,), math.log(n))
+    out = sa.sparse_attn(q.to(DEV), kv.to(DEV), sink.to(DEV), idx.to(DEV), 1.0)
+    torch.cuda.synchronize()
+    ref = kv[0, idx[0, 0].long()].double().mean(0) / (1.0 + math.exp(float(sink[0])) / n)
+    assert_close(out[0, 0].double().cpu().numpy(), ref.expand(128, D).numpy(), "sink halves")
+
+
+def test_order_invariance():
+    inp = _custom(2, 2, 128, 512, 400, 300, seed=9)
+    a = _run(inp)
+    perm = torch.randperm(300, generator=torch.Generator().manual_seed(1)).to(DEV)
+    inp2 = dict(inp)
+    inp2["topk_idxs"] = inp["topk_idxs"][:, :, perm].contiguous()
+    b = _run(inp2)
+    torch.cuda.synchronize()
+    assert_close(to64(a), to64(b), "order invariance")
+
+
+def test_out_of_range_indices_are_empty():
+    inp = _custom(1, 2, 16, 64, 100, 48, seed=12)
+    a_idx = inp["topk_idxs"].clone()
+    a_idx[:, :, 0] = 100  # == T
+    a_idx[:, :, 1] = -5
+    a_idx[:, :, 2] = 2**30
+    b_idx = a_idx.clone()
+    b_idx[:, :, :3] = -1
+    inp["topk_idxs"] = a_idx
+    a = _run(inp)
+    inp["topk_idxs"] = b_idx
+    b = _run(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_write_bounds_guard_band():
+    """Guard bands around out keep their sentinel."""
+    inp = _custom(2, 3, 128, 512, 200, 100, seed=13)
+    B, S, H, D = inp["q"].shape
+    n = B * S * H * D
+    buf = torch.full((n + 2 * 4096,), 3.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[4096:4096 + n].view(B, S, H, D)
+    for splits in (1, 2):
+        _run(inp, out=out, num_splits=splits)
+        torch.cuda.synchronize()
+        assert (buf[:4096] == 3.0).all() and (buf[4096 + n:] == 3.0).all()
+
+
+@pytest.mark.parametrize("cfg", ["decode"])
+def test_decode_config_sampled(oracle_impl, cfg):
+    inp = wl.sparse_inputs(cfg, 1002, DEV)
+    out = _run(inp)
+    torch.cuda.synchronize()
+    B, S = inp["q"].shape[:2]
+    tokens = np.arange(0, B * S, 4)
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"], tokens)
+    got = to64(out.reshape(B * S, *out.shape[2:])[torch.as_tensor(tokens, device=DEV)])
+    assert_close(got, ref, cfg)
+
+
+def test_prefill_config_sampled(oracle_impl):
+    inp = wl.sparse_inputs("prefill", 1003, DEV)
+    out = _run(inp)
+    torch.cuda.synchronize()
+    tokens = np.array([0, 1, 2, 127, 128, 129, 511, 1000, 2047, 3000, 4094, 4095])
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"], tokens)
+    got = to64(out[0][torch.as_tensor(tokens, device=DEV)])
+    assert_close(got, ref, "prefill")
+
+
+def test_ragged_config_sampled(oracle_impl):
+    inp = wl.sparse_inputs("ragged", 1005, DEV)
+    out = _run(inp)
+    torch.cuda.synchronize()
+    tokens = np.arange(0, 32, 3)
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"], tokens)
+    got = to64(out.reshape(32, *out.shape[2:])[torch.as_tensor(tokens, device=DEV)])
+    assert_close(got, ref, "ragged")
+    del inp
+
+
+def test_graph_replay_tracks_new_indices(oracle_impl):
+    """Capture once, replay with new index lists (grid depends only on shapes)."""
+    inp = _custom(4, 1, 128, 512, 600, 320, seed=21)
+    out = torch.empty_like(inp["q"])
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(4, 1, 128, 512, 320) + 256, dtype=torch.uint8, device=DEV)
+    ws = ws[(-ws.data_ptr()) % 256:]
+    _run(inp, out=out, workspace=ws)  # warm up outside the graph
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _run(inp, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        new = _custom(4, 1, 128, 512, 600, 320, seed=100 + rep, holes=0.3 * rep)
+        inp["topk_idxs"].copy_(new["topk_idxs"])
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+        assert_close(to64(out).reshape(ref.shape), ref, f"replay {rep}")

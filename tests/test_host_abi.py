@@ -1,0 +1,120 @@
+"""The C-ABI library without a GPU: it loads, exports what include/sparse_attn.h declares,
+computes the mask shape on the host, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_sparse_attention_attn_amd as sa
+from top_sparse_attention_attn_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "defined"})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(api.library_path())
+    names = declared_functions()
+    assert set(names) >= set(api.EXPORTED), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_mask_shape_rule_matches_pages_example():
+    # prhub summary of vLLM PR #52217, test_topk_mask_rows_are_aligned_for_vectorized_loads
+    assert sa.topk_bitmask_shape(2, 129, 129) == (2, 256, 8)
+    assert sa.topk_bitmask_shape(2, 129, 129, True) == (2, 256, 8)
+    assert sa.topk_bitmask_shape(1, 1, 129)[2] == 8
+
+
+def test_mask_shape_matches_oracle(oracle_impl):
+    for args in [(1, 0, 0, False), (3, 128, 8192, False), (3, 129, 8192, True), (2, 257, 31, True), (1, 1, 1, False),
+                 (4, 2048, 8192, False), (2, 100, 262144, True)]:
+        assert sa.topk_bitmask_shape(*args) == oracle_impl.topk_mask_shape(*args), args
+
+
+def _lib():
+    return api._load()
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # never dereferenced: every call below is rejected first
+FAKE_ODD = ctypes.c_void_p((1 << 20) + 8)
+
+
+def _sparse(q=FAKE, kv=FAKE, sink=FAKE, idx=FAKE, out=FAKE, B=1, S=1, H=8, D=64, T=16, K=8, splits=0, ws=None, wsb=0):
+    return _lib().sparse_attn_fwd(q, kv, sink, idx, out, B, S, H, D, T, K, 0.125, splits, ws, wsb, None)
+
+
+def test_sparse_rejects_before_any_hip_call():
+    assert _sparse(D=100) == 4                      # unsupported head dim
+    assert _sparse(H=129) == 4                      # too many heads
+    assert _sparse(B=-1) == 2
+    assert _sparse(splits=-1) == 2
+    assert _sparse(q=None) == 1
+    assert _sparse(idx=None) == 1
+    assert _sparse(q=FAKE_ODD) == 3                 # q not 16-byte aligned
+    # decode-like shape that needs a workspace, none given
+    assert _sparse(B=64, H=128, D=512, T=8320, K=1152) == 5
+    # empty work is accepted without a launch
+    assert _sparse(B=0) == 0
+    assert _sparse(S=0, q=None, out=None) == 0
+
+
+def test_workspace_policy():
+    assert sa.sparse_attn_num_splits(64, 1, 128, 512, 1152) == 4
+    assert sa.sparse_attn_num_splits(1, 4096, 128, 512, 1152) == 1
+    assert sa.sparse_attn_num_splits(1, 4, 8, 64, 32) == 1
+    assert sa.sparse_attn_workspace_bytes(1, 4096, 128, 512, 1152) == 0
+    w = sa.sparse_attn_workspace_bytes(64, 1, 128, 512, 1152)
+    assert w == 64 * 4 * 128 * (512 + 2) * 4
+    assert sa.sparse_attn_workspace_bytes(64, 1, 128, 512, 1152, 2) == 64 * 2 * 128 * (512 + 2) * 4
+
+
+def _mask(idx=FAKE, ql=None, ks=None, m=FAKE, B=1, Q=4, topk=8, key_len=100, pq=128, W=4):
+    return _lib().topk_bitmask_build(idx, ql, ks, m, B, Q, topk, key_len, pq, W, None)
+
+
+def test_bitmask_rejects_before_any_hip_call():
+    assert _mask(W=6) == 2            # words not a multiple of 4
+    assert _mask(key_len=200) == 2    # 32 * words < key_len
+    assert _mask(pq=2) == 2           # padded_q < Q
+    assert _mask(ks=FAKE, key_len=128) == 2  # no room for the reserved word
+    assert _mask(m=None) == 1
+    assert _mask(m=FAKE_ODD) == 3
+    assert _mask(B=0) == 0
+
+
+def _masked(q=FAKE, k=FAKE, v=FAKE, m=FAKE, o=FAKE, B=1, Q=4, KV=64, H=2, Dqk=192, Dv=128, pq=128, W=4, bits=128):
+    return _lib().masked_attn_fwd(q, k, v, m, o, B, Q, KV, H, Dqk, Dv, pq, W, 0.1, bits, None)
+
+
+def test_masked_rejects_before_any_hip_call():
+    assert _masked(Dqk=128) == 4
+    assert _masked(bits=64) == 2
+    assert _masked(W=1) == 2
+    assert _masked(KV=200) == 2       # mask too narrow for the keys
+    assert _masked(o=None) == 1
+    assert _masked(k=FAKE_ODD) == 3
+    assert _masked(Q=0) == 0
+
+
+def test_status_strings():
+    for s in range(7):
+        assert _lib().sa_status_string(s)
+    assert _lib().sa_status_string(99) == b"unknown status"
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sa.sparse_attn(q, torch.zeros(1, 4, 64, dtype=torch.bfloat16), torch.zeros(8), torch.zeros(1, 1, 2, dtype=torch.int32),
+                       0.125)

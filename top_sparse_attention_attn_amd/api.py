@@ -1,0 +1,212 @@
+"""Python binding of libsparse_attn.so (declared in include/sparse_attn.h).
+
+Argument marshalling only: every entry point checks dtypes/devices/contiguity of
+the torch tensors, passes their device pointers and the current HIP stream to
+the C ABI, and raises SparseAttnError on a nonzero status. All computation runs
+in the library's kernels; if the library cannot be loaded the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+_lib = None
+_lock = threading.Lock()
+
+SA_STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_ALIGN", 4: "SA_ERR_UNSUPPORTED",
+             5: "SA_ERR_WORKSPACE", 6: "SA_ERR_HIP"}
+
+EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_fwd",
+            "topk_bitmask_shape", "topk_bitmask_build", "masked_attn_fwd"]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _load().sa_status_string(status).decode() if _lib is not None else ""
+        super().__init__(f"{fn} failed: {SA_STATUS.get(status, status)} ({msg})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m top_sparse_attention_attn_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        lib.sa_status_string.argtypes = [I]
+        lib.sa_status_string.restype = ctypes.c_char_p
+        lib.sparse_attn_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
+        lib.sparse_attn_workspace_bytes.restype = ctypes.c_size_t
+        lib.sparse_attn_num_splits.argtypes = [I64, I64, I64, I64, I64]
+        lib.sparse_attn_num_splits.restype = I
+        lib.sparse_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
+        lib.sparse_attn_fwd.restype = I
+        lib.topk_bitmask_shape.argtypes = [I64, I64, I64, I, P]
+        lib.topk_bitmask_shape.restype = I
+        lib.topk_bitmask_build.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P]
+        lib.topk_bitmask_build.restype = I
+        lib.masked_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, F, I, P]
+        lib.masked_attn_fwd.restype = I
+        _lib = lib
+        return lib
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _call(fn_name: str, *args):
+    rc = getattr(_load(), fn_name)(*args)
+    if rc != 0:
+        raise SparseAttnError(fn_name, rc)
+
+
+# --------------------------------------------------------------------------- sparse attention
+_ws_cache: dict = {}
+
+
+def sparse_attn_num_splits(B: int, S: int, H: int, D: int, K: int) -> int:
+    return int(_load().sparse_attn_num_splits(B, S, H, D, K))
+
+
+def sparse_attn_workspace_bytes(B: int, S: int, H: int, D: int, K: int, num_splits: int = 0) -> int:
+    return int(_load().sparse_attn_workspace_bytes(B, S, H, D, K, num_splits))
+
+
+def _workspace(device: torch.device, nbytes: int, workspace: torch.Tensor | None):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, device)
+        return workspace, workspace.numel()
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    off = (-ws.data_ptr()) % 256
+    view = ws[off:off + nbytes]
+    return view, view.numel()
+
+
+def sparse_attn(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor, topk_idxs: torch.Tensor,
+                scale: float, out: torch.Tensor | None = None, num_splits: int = 0,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """o = sparse_attn(q, kv, attn_sink, topk_idxs, scale).
+
+    q [B,S,H,D] bf16, kv [B,T,D] bf16, attn_sink [H] fp32, topk_idxs [B,S,K] int32
+    (-1 = empty slot); returns o [B,S,H,D] bf16. num_splits = 0 lets the library choose.
+    """
+    dev = q.device
+    _check(q, "q", torch.bfloat16)
+    _check(kv, "kv", torch.bfloat16, dev)
+    _check(attn_sink, "attn_sink", torch.float32, dev)
+    _check(topk_idxs, "topk_idxs", torch.int32, dev)
+    if q.dim() != 4 or kv.dim() != 3 or topk_idxs.dim() != 3 or attn_sink.dim() != 1:
+        raise ValueError("expected q [B,S,H,D], kv [B,T,D], attn_sink [H], topk_idxs [B,S,K]")
+    B, S, H, D = q.shape
+    T = kv.shape[1]
+    K = topk_idxs.shape[2]
+    if kv.shape[0] != B or kv.shape[2] != D or attn_sink.shape[0] != H or tuple(topk_idxs.shape[:2]) != (B, S):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    need = sparse_attn_workspace_bytes(B, S, H, D, K, num_splits)
+    ws, ws_bytes = _workspace(dev, need, workspace)
+    _call("sparse_attn_fwd", _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, S, H, D, T, K,
+          float(scale), int(num_splits), _ptr(ws), ws_bytes, _stream_ptr(dev))
+    return out
+
+
+# --------------------------------------------------------------------------- bit mask
+def topk_bitmask_shape(B: int, max_q_len: int, max_key_len: int, reserve_key_start_word: bool = False):
+    arr = (ctypes.c_int64 * 3)()
+    _call("topk_bitmask_shape", B, max_q_len, max_key_len, int(bool(reserve_key_start_word)), arr)
+    return int(arr[0]), int(arr[1]), int(arr[2])
+
+
+def topk_bitmask_build(topk_idxs: torch.Tensor, key_len: int, q_lens: torch.Tensor | None = None,
+                       key_starts: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Bit-packed mask [B, padded_q, words] (uint32 bits stored as int32) for topk_idxs [B, Q, topk] int32."""
+    dev = topk_idxs.device
+    _check(topk_idxs, "topk_idxs", torch.int32)
+    if topk_idxs.dim() != 3:
+        raise ValueError("topk_idxs must be [B, Q, topk]")
+    B, Q, topk = topk_idxs.shape
+    if q_lens is not None:
+        _check(q_lens, "q_lens", torch.int32, dev)
+    if key_starts is not None:
+        _check(key_starts, "key_starts", torch.int32, dev)
+    if out is None:
+        shape = topk_bitmask_shape(B, Q, key_len, key_starts is not None)
+        out = torch.empty(shape, dtype=torch.int32, device=dev)
+    else:
+        _check(out, "out", torch.int32, dev)
+        if out.dim() != 3 or out.shape[0] != B:
+            raise ValueError("out must be [B, padded_q, words]")
+    _call("topk_bitmask_build", _ptr(topk_idxs), _ptr(q_lens), _ptr(key_starts), _ptr(out), B, Q, topk, int(key_len),
+          out.shape[1], out.shape[2], _stream_ptr(dev))
+    return out
+
+
+# --------------------------------------------------------------------------- masked attention
+def masked_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor | None, scale: float,
+                mask_load_bits: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense attention over the keys whose mask bit is set (mask None = all keys).
+
+    q [B,Q,H,192], k [B,KV,H,192], v [B,KV,H,128] bf16; mask [B,padded_q,words] int32/uint32 bits.
+    """
+    dev = q.device
+    _check(q, "q", torch.bfloat16)
+    _check(k, "k", torch.bfloat16, dev)
+    _check(v, "v", torch.bfloat16, dev)
+    B, Q, H, Dqk = q.shape
+    KV, Dv = k.shape[1], v.shape[3]
+    if k.shape != (B, KV, H, Dqk) or tuple(v.shape[:3]) != (B, KV, H):
+        raise ValueError("inconsistent shapes")
+    padded_q = words = 0
+    if mask is not None:
+        _check(mask, "mask", torch.int32, dev)
+        if mask.dim() != 3 or mask.shape[0] != B:
+            raise ValueError("mask must be [B, padded_q, words]")
+        padded_q, words = mask.shape[1], mask.shape[2]
+    if out is None:
+        out = torch.empty((B, Q, H, Dv), dtype=torch.bfloat16, device=dev)
+    else:
+        _check(out, "out", torch.bfloat16, dev)
+    _call("masked_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out), B, Q, KV, H, Dqk, Dv, padded_q, words,
+          float(scale), int(mask_load_bits), _stream_ptr(dev))
+    return out

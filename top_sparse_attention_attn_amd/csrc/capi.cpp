@@ -1,0 +1,153 @@
+// Host side of the C ABI declared in include/sparse_attn.h: argument checks (done before
+// any HIP call, so a rejected call touches no memory), split and workspace policy, and
+// dispatch to the kernel launchers.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sparse_attn.h"
+
+extern "C" {
+int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
+                              int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
+                              int nsplit, void* ws, void* stream);
+int sa_internal_head_blocks(int64_t H);
+int sa_internal_launch_bitmask(const int32_t* idx, const int32_t* q_lens, const int32_t* key_starts, uint32_t* mask,
+                               int64_t B, int64_t Q, int64_t topk, int64_t key_len, int64_t padded_q, int64_t words,
+                               void* stream);
+int64_t sa_internal_bitmask_max_words(void);
+int sa_internal_launch_masked(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
+                              int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
+                              int64_t words, float scale, int mask_load_bits, void* stream);
+}
+
+namespace {
+
+constexpr int kTileRows = 32;   // slot tile of the sparse kernel
+constexpr int kMaxSplits = 16;  // combine kernel limit
+constexpr int64_t kTargetWorkgroups = 256;  // one per CU on MI355X
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool sparse_sizes_ok(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K) {
+  return B >= 0 && S >= 0 && H >= 0 && D >= 0 && K >= 0;
+}
+
+int choose_splits(int64_t B, int64_t S, int64_t K, int requested) {
+  const int64_t ntok = B * S;
+  const int64_t tiles = cdiv(K, kTileRows);
+  if (ntok <= 0 || tiles <= 0) return 1;
+  int64_t n = requested > 0 ? requested : cdiv(kTargetWorkgroups, ntok);
+  if (n > kMaxSplits) n = kMaxSplits;
+  if (n > tiles) n = tiles;
+  if (n < 1) n = 1;
+  return (int)n;
+}
+
+size_t sparse_ws_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const int64_t hp = (int64_t)sa_internal_head_blocks(H) * 16;
+  const int64_t pairs = B * S * nsplit;
+  return (size_t)(pairs * hp * D + pairs * hp * 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_NULL: return "a required pointer is NULL";
+    case SA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case SA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SA_ERR_UNSUPPORTED: return "unsupported head dimension or head count";
+    case SA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int sparse_attn_num_splits(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K) {
+  if (!sparse_sizes_ok(B, S, H, D, K)) return 1;
+  return choose_splits(B, S, K, 0);
+}
+
+size_t sparse_attn_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K, int num_splits) {
+  if (!sparse_sizes_ok(B, S, H, D, K) || num_splits < 0) return 0;
+  if (H < 1 || H > 128) return 0;
+  return sparse_ws_bytes(B, S, H, D, choose_splits(B, S, K, num_splits));
+}
+
+int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                    int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sparse_sizes_ok(B, S, H, D, K) || T < 0 || num_splits < 0 || num_splits > 64) return SA_ERR_SHAPE;
+  if (B * S == 0 || H == 0) return SA_OK;
+  if (D != 64 && D != 512) return SA_ERR_UNSUPPORTED;
+  if (H > 128) return SA_ERR_UNSUPPORTED;
+  if (B * S > (int64_t)1 << 30 || T > (int64_t)1 << 31 || K > (int64_t)1 << 30) return SA_ERR_SHAPE;
+  if (!q || !attn_sink || !out || (K > 0 && !topk_idxs) || (T > 0 && K > 0 && !kv)) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (kv && !aligned16(kv))) return SA_ERR_ALIGN;
+  if (((uintptr_t)attn_sink & 3u) || (topk_idxs && ((uintptr_t)topk_idxs & 3u))) return SA_ERR_ALIGN;
+  const int nsplit = choose_splits(B, S, K, num_splits);
+  const size_t need = sparse_ws_bytes(B, S, H, D, nsplit);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return SA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255u) return SA_ERR_ALIGN;
+  }
+  const int rc = sa_internal_launch_sparse(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, nsplit,
+                                           need > 0 ? workspace : nullptr, stream);
+  return rc == 0 ? SA_OK : SA_ERR_HIP;
+}
+
+int topk_bitmask_shape(int64_t B, int64_t max_q_len, int64_t max_key_len, int reserve_key_start_word,
+                       int64_t* out_shape) {
+  if (!out_shape) return SA_ERR_NULL;
+  if (B < 0 || max_q_len < 0 || max_key_len < 0) return SA_ERR_SHAPE;
+  const int64_t tile_m = max_q_len <= 128 ? 128 : 256;
+  const int64_t words = cdiv(cdiv(max_key_len, 32) + (reserve_key_start_word ? 1 : 0), 4) * 4;
+  out_shape[0] = B;
+  out_shape[1] = cdiv(max_q_len, tile_m) * tile_m;
+  out_shape[2] = words;
+  return SA_OK;
+}
+
+int topk_bitmask_build(const int32_t* topk_idxs, const int32_t* q_lens, const int32_t* key_starts, uint32_t* mask,
+                       int64_t B, int64_t Q, int64_t topk, int64_t key_len, int64_t padded_q, int64_t words,
+                       void* stream) {
+  if (B < 0 || Q < 0 || topk < 0 || key_len < 0 || padded_q < 0 || words < 0) return SA_ERR_SHAPE;
+  if (padded_q < Q || words % 4 != 0 || 32 * words < key_len) return SA_ERR_SHAPE;
+  if (key_starts && (words < cdiv(key_len, 32) + 1 || padded_q < 1)) return SA_ERR_SHAPE;
+  if (B * padded_q == 0 || words == 0) return SA_OK;
+  if (words > sa_internal_bitmask_max_words()) return SA_ERR_UNSUPPORTED;
+  if (B * padded_q > ((int64_t)1 << 31) - 1 || B * Q * topk > ((int64_t)1 << 40)) return SA_ERR_SHAPE;
+  if (!mask || (Q > 0 && topk > 0 && !topk_idxs)) return SA_ERR_NULL;
+  if (!aligned16(mask)) return SA_ERR_ALIGN;
+  if ((topk_idxs && ((uintptr_t)topk_idxs & 3u)) || (q_lens && ((uintptr_t)q_lens & 3u)) ||
+      (key_starts && ((uintptr_t)key_starts & 3u)))
+    return SA_ERR_ALIGN;
+  const int rc = sa_internal_launch_bitmask(topk_idxs, q_lens, key_starts, mask, B, Q, topk, key_len, padded_q,
+                                            words, stream);
+  return rc == 0 ? SA_OK : SA_ERR_HIP;
+}
+
+int masked_attn_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, int64_t B,
+                    int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q, int64_t words,
+                    float scale, int mask_load_bits, void* stream) {
+  if (B < 0 || Q < 0 || KV < 0 || H < 0 || Dqk < 0 || Dv < 0 || padded_q < 0 || words < 0) return SA_ERR_SHAPE;
+  if (mask_load_bits != 128 && mask_load_bits != 32) return SA_ERR_SHAPE;
+  if (B * Q * H == 0) return SA_OK;
+  if (Dqk != 192 || Dv != 128) return SA_ERR_UNSUPPORTED;
+  if (mask && (padded_q < Q || words % 4 != 0 || 32 * words < KV)) return SA_ERR_SHAPE;
+  if (B * H * cdiv(Q, 128) > ((int64_t)1 << 31) - 1 || KV > ((int64_t)1 << 30)) return SA_ERR_SHAPE;
+  if (!q || !out || (KV > 0 && (!k || !v))) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (k && !aligned16(k)) || (v && !aligned16(v)) || (mask && !aligned16(mask)))
+    return SA_ERR_ALIGN;
+  const int rc = sa_internal_launch_masked(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale,
+                                           mask_load_bits, stream);
+  return rc == 0 ? SA_OK : (rc == 2 ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
+}
+
+}  // extern "C"

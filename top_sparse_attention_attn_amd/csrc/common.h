@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// s_waitcnt with vmcnt = VM (0..63), lgkmcnt = 0, expcnt untouched.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+// s_waitcnt lgkmcnt(0) only (vector memory left in flight).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8)); }
+
+// Wait until at most `n` vector-memory operations of this wave are outstanding (n clamped to 0..16).
+__device__ __forceinline__ void wait_vm_lgkm0_dyn(int n) {
+  switch (n <= 0 ? 0 : (n >= 16 ? 16 : n)) {
+    case 0: wait_vm_lgkm0<0>(); break;
+    case 1: wait_vm_lgkm0<1>(); break;
+    case 2: wait_vm_lgkm0<2>(); break;
+    case 3: wait_vm_lgkm0<3>(); break;
+    case 4: wait_vm_lgkm0<4>(); break;
+    case 5: wait_vm_lgkm0<5>(); break;
+    case 6: wait_vm_lgkm0<6>(); break;
+    case 7: wait_vm_lgkm0<7>(); break;
+    case 8: wait_vm_lgkm0<8>(); break;
+    case 9: wait_vm_lgkm0<9>(); break;
+    case 10: wait_vm_lgkm0<10>(); break;
+    case 11: wait_vm_lgkm0<11>(); break;
+    case 12: wait_vm_lgkm0<12>(); break;
+    case 13: wait_vm_lgkm0<13>(); break;
+    case 14: wait_vm_lgkm0<14>(); break;
+    case 15: wait_vm_lgkm0<15>(); break;
+    default: wait_vm_lgkm0<16>(); break;
+  }
+}
+
+// Workgroup barrier that also stops the compiler from moving memory accesses across it.
+// It does not wait for outstanding memory operations; callers issue the s_waitcnt they need.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4r+c supplies
+// the address of 4 consecutive 16-bit values (columns 4c..4c+3 of row r of a 4x16 block);
+// lane n of the group receives column n of rows 0..3.
+__device__ __forceinline__ v4i16 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(const lds_void_t*)p);
+}
+
+__device__ __forceinline__ bf16x8 concat_tr(const v4i16& lo, const v4i16& hi) {
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
+
+// Cross-lane xor shuffle within a wave (lanes l and l^mask).
+__device__ __forceinline__ float xor_shuffle(float v, int mask) {
+  int lane = __lane_id();
+  int src = lane ^ mask;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+// Map a linear workgroup id so that consecutive logical ids land on the same XCD
+// (workgroups are dispatched round-robin over the 8 XCDs).
+__device__ __forceinline__ int xcd_local_id(int id, int n) {
+  return (n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id;
+}
+
+}  // namespace sa

@@ -1,0 +1,467 @@
+// Top-k sparse attention on gfx950.
+//
+// What is computed ("DeepSeek V4 源码剖析", ch. 5, sections 5.2, 5.4, 5.5): for every
+// token and head, a softmax over the scaled dot products with the K gathered rows
+// kv[b, idx] (empty slots excluded) plus one sink logit, applied to the same rows; the
+// sink takes part in the normalisation only.
+//
+// Work decomposition (MI355X-specific; the pages' kernels are prior art only):
+//  * One workgroup per (token, slot range) covering ALL heads of the token, so every
+//    gathered row is pulled from HBM into LDS once and used by all heads. When there
+//    are too few tokens to fill the 256 CUs a token's slots are cut into `nsplit`
+//    ranges, merged afterwards by a small kernel that adds the sink exactly once.
+//  * Rows arrive in 32-row tiles through a 4-deep ring of LDS buffers, written by
+//    global_load_lds (16 bytes per lane, one 1 KB row per wave instruction) straight
+//    from memory, two tiles ahead of the tile whose scores are being computed.
+//  * 8 waves, 2 per SIMD, in two roles that run one tile apart:
+//      score waves (0-3) keep the queries of two 16-head blocks in registers, compute
+//        S^T = K Q^T for tile t with MFMA 16x16x32 bf16 and the online softmax, write
+//        the bf16 weights P to LDS, then add their share of P V for tile t-1;
+//      value waves (4-7) add the rest of P V for tile t-1.
+//    Every wave owns a slice of the head dimension of the output for all heads; V is
+//    read with the transposing LDS read (ds_read_b64_tr_b16). One barrier per tile.
+//  * Online softmax in base 2 with a lazily moved reference maximum: the output is
+//    rescaled only when a head's maximum grows by more than 2^8 (rare after the first
+//    tile); weights stay <= 2^8, so nothing overflows.
+#include "common.h"
+
+namespace sa {
+
+constexpr int kTile = 32;       // rows per tile
+constexpr int kBufs = 4;        // LDS ring depth (tiles t-1 .. t+2)
+constexpr float kLazy = 8.0f;   // reference-max slack, log2 units
+constexpr int kMaxSplits = 16;
+constexpr int kThreads = 512;
+constexpr int kPStride = kTile + 8;  // bf16 elements per P row in LDS (80 bytes)
+
+template <int D>
+struct Geo {
+  static constexpr int kRowStride = D * 2 + 16;  // padded LDS row: spreads rows over banks
+  static constexpr int kBufBytes = kTile * kRowStride;
+  static constexpr int kDSteps = D / 32;         // QK MFMA steps over the head dimension
+  static constexpr int kLanesPerRow = D / 8;     // 16-byte chunks per row
+  static constexpr int kNDB = D / 16;            // 16-column output blocks
+  static constexpr int kDBA = kNDB >= 32 ? kNDB / 16 : 1;  // blocks per score wave
+  static constexpr int kDBB = (kNDB - 4 * kDBA) / 4;         // blocks per value wave
+  static_assert(kNDB % 4 == 0 && kDBB >= 0, "head dimension must be a multiple of 64");
+};
+
+template <int D, int HB>
+struct Smem {
+  unsigned char kv[kBufs][Geo<D>::kBufBytes];
+  __bf16 p[2][HB * 16 * kPStride];
+  float alpha[2][HB * 16];
+  float fin[HB * 16];
+  unsigned char vmb[kBufs][8];  // per wave: validity of its 4 rows of the tile (one byte each)
+  int flag[2][4];
+};
+
+// 32-bit validity mask of a tile's rows (bit j = row j holds a gathered row).
+template <int D, int HB>
+__device__ __forceinline__ unsigned tile_mask(const Smem<D, HB>& sm, int bi) {
+  const uint2 v = *(const uint2*)(&sm.vmb[bi][0]);
+  auto nib = [](unsigned x) {
+    return (x & 0xFu) | ((x >> 4) & 0xF0u) | ((x >> 8) & 0xF00u) | ((x >> 12) & 0xF000u);
+  };
+  return nib(v.x) | (nib(v.y) << 16);
+}
+
+// Output slice of one wave: NB column blocks starting at block DB0.
+template <int D, int HB, int NB>
+__device__ __forceinline__ void pv_step(Smem<D, HB>& sm, f32x4 (&oacc)[HB][NB > 0 ? NB : 1], int db0, int tp, int lane,
+                                        int g, int l16) {
+  using G = Geo<D>;
+  if constexpr (NB > 0) {
+    const int par = tp & 1;
+    const int bi = tp % kBufs;
+    if (sm.flag[par][0] | sm.flag[par][1] | sm.flag[par][2] | sm.flag[par][3]) {
+#pragma unroll
+      for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float a = sm.alpha[par][hb * 16 + 4 * g + i];
+#pragma unroll
+          for (int db = 0; db < NB; db++) oacc[hb][db][i] *= a;
+        }
+    }
+    // V operands of this wave's column blocks (transposed reads), then one P operand per
+    // head block: keeps at most one P operand live.
+    const int r4 = (lane >> 2) & 3, c4 = lane & 3;
+    const unsigned char* vbase = &sm.kv[bi][(8 * g + r4) * G::kRowStride + (db0 * 16 + 4 * c4) * 2];
+    bf16x8 bv[NB];
+#pragma unroll
+    for (int db = 0; db < NB; db++) {
+      const unsigned char* p0 = vbase + db * 32;
+      bv[db] = concat_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * G::kRowStride));
+    }
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++) {
+      const bf16x8 pa = *(const bf16x8*)(&sm.p[par][(hb * 16 + l16) * kPStride + 8 * g]);
+#pragma unroll
+      for (int db = 0; db < NB; db++) oacc[hb][db] = mfma16x16x32(pa, bv[db], oacc[hb][db]);
+    }
+  }
+}
+
+template <int D, int HB, bool SCORE>
+__device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
+                                          const float* __restrict__ sink, const int* __restrict__ idx,
+                                          __bf16* __restrict__ out, float* __restrict__ ws_o,
+                                          float* __restrict__ ws_ml, int S, int H, int T, int K, int nsplit,
+                                          float scale_log2) {
+  using G = Geo<D>;
+  constexpr int HP = HB * 16;
+  constexpr int NB = SCORE ? G::kDBA : G::kDBB;  // output column blocks of this wave
+  constexpr int NBX = NB > 0 ? NB : 1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int sw = wave & 3;  // index within the role
+  const int db0 = SCORE ? sw * G::kDBA : 4 * G::kDBA + sw * G::kDBB;
+
+  const int pair = xcd_local_id(blockIdx.x, gridDim.x);
+  const int tok = pair / nsplit, split = pair % nsplit;
+  const int b = tok / S;
+  const int ntiles_all = (K + kTile - 1) / kTile;
+  const int t0 = (int)(((long)split * ntiles_all) / nsplit);
+  const int ntl = (int)(((long)(split + 1) * ntiles_all) / nsplit) - t0;
+  const int* __restrict__ idx_tok = idx + (size_t)tok * K;
+  const __bf16* __restrict__ kv_b = kv + (size_t)b * T * D;
+
+  // ---- score waves: queries of head blocks sw and sw+4 (B operand of S^T = K Q^T)
+  constexpr int QB = SCORE ? (HB > 4 ? 2 : 1) : 1;
+  const int nq = SCORE ? ((sw + 4 < HB) ? 2 : ((sw < HB) ? 1 : 0)) : 0;
+  bf16x8 qreg[QB][SCORE ? G::kDSteps : 1];
+  float m_ref[QB], l_part[QB];
+  if constexpr (SCORE) {
+#pragma unroll
+    for (int qi = 0; qi < QB; qi++) {
+      const int h = (sw + 4 * qi) * 16 + l16;
+#pragma unroll
+      for (int s = 0; s < G::kDSteps; s++) {
+        bf16x8 v = {};
+        if (qi < nq && h < H) v = *(const bf16x8*)(q + ((size_t)tok * H + h) * D + 32 * s + 8 * g);
+        qreg[qi][s] = v;
+      }
+      m_ref[qi] = kNegInf;
+      l_part[qi] = 0.f;
+    }
+    // Let the query loads land before any row DMA is issued, so that no wait for them is
+    // left inside the tile loop (it would also drain the DMA queue).
+    wait_vm_lgkm0<0>();
+  }
+
+  f32x4 oacc[HB][NBX];
+#pragma unroll
+  for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+    for (int db = 0; db < NBX; db++) oacc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- row gather: wave w owns rows 4w .. 4w+3 of every tile
+  auto load_rows = [&](int tt, int (&rows)[4]) {
+    const int slot0 = (t0 + tt) * kTile + wave * 4;
+    if (slot0 + 4 <= K) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) rows[r] = idx_tok[slot0 + r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; r++) rows[r] = (slot0 + r < K) ? idx_tok[slot0 + r] : -1;
+    }
+  };
+  auto issue = [&](int tt, const int (&rows)[4]) -> int {  // returns DMA instructions issued
+    const int bi = tt % kBufs;
+    unsigned vbits = 0;
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int row = rows[r];
+      unsigned char* dst = &sm.kv[bi][(wave * 4 + r) * G::kRowStride];
+      if (row >= 0 && row < T) {
+        vbits |= 1u << r;
+        n++;
+        if (lane < G::kLanesPerRow)
+          __builtin_amdgcn_global_load_lds((const void*)(kv_b + (size_t)row * D + lane * 8), (lds_void_t*)dst, 16, 0,
+                                           0);
+      } else if (lane < G::kLanesPerRow) {
+        *(uint4*)(dst + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if (lane == 0) sm.vmb[bi][wave] = (unsigned char)vbits;  // own byte: no clearing needed
+    return n;
+  };
+
+  int rows_next[4];
+  int dma_last = 0;  // DMA count of the most recently issued tile
+  if (threadIdx.x < 8) (&sm.flag[0][0])[threadIdx.x] = 0;
+  wait_lgkm0();
+  wg_barrier();
+  for (int tt = 0; tt < 2 && tt < ntl; tt++) {
+    int rows[4];
+    load_rows(tt, rows);
+    dma_last = issue(tt, rows);
+  }
+  if (2 < ntl) load_rows(2, rows_next);
+
+  for (int tt = 0; tt <= ntl; tt++) {
+    // Tile tt's rows have landed once only the younger tile's DMAs may still be pending.
+    wait_vm_lgkm0_dyn(tt + 1 < ntl ? dma_last : 0);
+    wg_barrier();  // tile tt and P(tt-1) visible; everyone is done with tile tt-2 and P(tt-2)
+    // ---- prefetch tile tt+2 into the buffer freed by tile tt-2
+    if (tt + 2 < ntl) {
+      dma_last = issue(tt + 2, rows_next);
+      if (tt + 3 < ntl) load_rows(tt + 3, rows_next);
+    }
+    if constexpr (SCORE) {
+      if (tt < ntl) {
+        const int bi = tt % kBufs;
+        const int par = tt & 1;
+        const unsigned vm = tile_mask(sm, bi);
+        bool any_resc = false;
+        if (vm != 0u && nq > 0) {
+          const unsigned char* buf = sm.kv[bi];
+          f32x4 sacc[QB][2];
+#pragma unroll
+          for (int qi = 0; qi < QB; qi++) sacc[qi][0] = sacc[qi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < G::kDSteps; s++) {
+            const bf16x8 a0 = *(const bf16x8*)(buf + l16 * G::kRowStride + (32 * s + 8 * g) * 2);
+            const bf16x8 a1 = *(const bf16x8*)(buf + (16 + l16) * G::kRowStride + (32 * s + 8 * g) * 2);
+            sacc[0][0] = mfma16x16x32(a0, qreg[0][s], sacc[0][0]);
+            sacc[0][1] = mfma16x16x32(a1, qreg[0][s], sacc[0][1]);
+            if (QB > 1 && nq > 1) {
+              sacc[QB - 1][0] = mfma16x16x32(a0, qreg[QB - 1][s], sacc[QB - 1][0]);
+              sacc[QB - 1][1] = mfma16x16x32(a1, qreg[QB - 1][s], sacc[QB - 1][1]);
+            }
+          }
+#pragma unroll
+          for (int qi = 0; qi < QB; qi++) {
+            if (qi >= nq) break;
+            float x[2][4];
+            float tmax = kNegInf;
+#pragma unroll
+            for (int jb = 0; jb < 2; jb++)
+#pragma unroll
+              for (int i = 0; i < 4; i++) {
+                const int j = 16 * jb + 4 * g + i;
+                float v = sacc[qi][jb][i] * scale_log2;
+                v = ((vm >> j) & 1u) ? v : kNegInf;
+                x[jb][i] = v;
+                tmax = fmaxf(tmax, v);
+              }
+            tmax = fmaxf(tmax, xor_shuffle(tmax, 16));
+            tmax = fmaxf(tmax, xor_shuffle(tmax, 32));
+            const float mold = m_ref[qi];
+            const bool move = tmax > mold + kLazy;  // also true for the first finite maximum
+            const float mnew = move ? tmax : mold;
+            const float alpha = move ? exp2_fast(mold - mnew) : 1.f;
+            const bool resc = move && (mold > kNegInf);
+            any_resc |= resc;
+            m_ref[qi] = mnew;
+            float lsum = l_part[qi] * alpha;
+            const int h = (sw + 4 * qi) * 16 + l16;
+#pragma unroll
+            for (int jb = 0; jb < 2; jb++) {
+              bf16x4 pk;
+#pragma unroll
+              for (int i = 0; i < 4; i++) {
+                const float p = (mnew > kNegInf) ? exp2_fast(x[jb][i] - mnew) : 0.f;
+                const __bf16 pb = (__bf16)p;
+                pk[i] = pb;
+                lsum += (float)pb;
+              }
+              *(bf16x4*)(&sm.p[par][h * kPStride + 16 * jb + 4 * g]) = pk;
+            }
+            l_part[qi] = lsum;
+            if (g == 0) sm.alpha[par][h] = resc ? alpha : 1.f;
+          }
+        }
+        // Every score wave publishes its own rescale flag for this tile (no shared writes).
+        if (lane == 0) sm.flag[par][sw] = __any(any_resc) ? 1 : 0;
+      }
+    }
+    // ---- P V for the previous tile
+    if (tt >= 1) {
+      const int tp = tt - 1;
+      if (tile_mask(sm, tp % kBufs) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, lane, g, l16);
+    }
+  }
+
+  // ---- per-head totals (score waves): sum the partial row sums over the 4 lane groups
+  if constexpr (SCORE) {
+#pragma unroll
+    for (int qi = 0; qi < QB; qi++) {
+      l_part[qi] += xor_shuffle(l_part[qi], 16);
+      l_part[qi] += xor_shuffle(l_part[qi], 32);
+    }
+  }
+
+  if (nsplit == 1) {
+    // Fold the sink into the normalisation: o = O 2^(m-M) / (l 2^(m-M) + 2^(sink-M)).
+    if constexpr (SCORE) {
+#pragma unroll
+      for (int qi = 0; qi < QB; qi++) {
+        if (qi >= nq) break;
+        const int h = (sw + 4 * qi) * 16 + l16;
+        float f = 0.f;
+        if (h < H) {
+          const float sk = sink[h];
+          const float m = m_ref[qi];
+          if (__builtin_isnan(sk)) {
+            f = __builtin_nanf("");
+          } else if (sk == __builtin_huge_valf()) {
+            f = 0.f;
+          } else {
+            const float s2 = sk * kLog2e;
+            const float M = fmaxf(m, s2);
+            if (M > kNegInf) {
+              const float c = (m > kNegInf) ? exp2_fast(m - M) : 0.f;
+              const float L = l_part[qi] * c + ((s2 > kNegInf) ? exp2_fast(s2 - M) : 0.f);
+              f = c / L;
+            }
+          }
+        }
+        if (g == 0) sm.fin[h] = f;
+      }
+    }
+    wait_lgkm0();
+    wg_barrier();
+    if constexpr (NB > 0) {
+#pragma unroll
+      for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int h = hb * 16 + 4 * g + i;
+          if (h >= H) continue;
+          const float f = sm.fin[h];
+          __bf16* orow = out + ((size_t)tok * H + h) * D + db0 * 16 + l16;
+#pragma unroll
+          for (int db = 0; db < NB; db++) orow[db * 16] = (__bf16)(oacc[hb][db][i] * f);
+        }
+    }
+  } else {
+    // Partial results for the combine kernel: block (hb, db) of MFMA accumulators, 16 bytes
+    // per lane, at ws_o[pair][hb][db][lane].
+    if constexpr (NB > 0) {
+      f32x4* wo = (f32x4*)(ws_o + (size_t)pair * HP * D) + lane;
+#pragma unroll
+      for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+        for (int db = 0; db < NB; db++) wo[(hb * G::kNDB + db0 + db) * 64] = oacc[hb][db];
+    }
+    if constexpr (SCORE) {
+#pragma unroll
+      for (int qi = 0; qi < QB; qi++) {
+        if (qi >= nq) break;
+        const int h = (sw + 4 * qi) * 16 + l16;
+        if (g == 0) {
+          ws_ml[((size_t)pair * HP + h) * 2 + 0] = m_ref[qi];
+          ws_ml[((size_t)pair * HP + h) * 2 + 1] = l_part[qi];
+        }
+      }
+    }
+  }
+}
+
+template <int D, int HB>
+__global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kv, const float* __restrict__ sink,
+    const int* __restrict__ idx, __bf16* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    int S, int H, int T, int K, int nsplit, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) Smem<D, HB> sm;
+  if (threadIdx.x < 256)
+    run_split<D, HB, true>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, scale_log2);
+  else
+    run_split<D, HB, false>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, scale_log2);
+}
+
+// Merge the split partials of one token (log-sum-exp in base 2) and add the sink once.
+template <int D, int HB>
+__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const float* __restrict__ ws_o,
+                                                                   const float* __restrict__ ws_ml,
+                                                                   const float* __restrict__ sink,
+                                                                   __bf16* __restrict__ out, int H, int nsplit) {
+  using G = Geo<D>;
+  constexpr int HP = HB * 16;
+  __shared__ float wgt[kMaxSplits * HP];
+  const int tok = blockIdx.x;
+  for (int h = threadIdx.x; h < HP; h += blockDim.x) {
+    const float sk = h < H ? sink[h] : kNegInf;
+    const float s2 = sk * kLog2e;
+    float M = s2;
+    for (int p = 0; p < nsplit; p++) M = fmaxf(M, ws_ml[(((size_t)tok * nsplit + p) * HP + h) * 2]);
+    float L = (s2 > kNegInf && M > kNegInf) ? exp2_fast(s2 - M) : 0.f;
+    for (int p = 0; p < nsplit; p++) {
+      const float m = ws_ml[(((size_t)tok * nsplit + p) * HP + h) * 2];
+      const float l = ws_ml[(((size_t)tok * nsplit + p) * HP + h) * 2 + 1];
+      L += (m > kNegInf) ? l * exp2_fast(m - M) : 0.f;
+    }
+    for (int p = 0; p < nsplit; p++) {
+      const float m = ws_ml[(((size_t)tok * nsplit + p) * HP + h) * 2];
+      float w = (m > kNegInf && M > kNegInf) ? exp2_fast(m - M) / L : 0.f;
+      if (__builtin_isnan(sk)) w = __builtin_nanf("");
+      else if (sk == __builtin_huge_valf()) w = 0.f;
+      wgt[p * HP + h] = w;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, l16 = lane & 15;
+  constexpr int NBLK = HB * G::kNDB;  // (hb, db) blocks of 64 lanes x 4 floats
+  for (int blk = threadIdx.x >> 6; blk < NBLK; blk += blockDim.x >> 6) {
+    const int hb = blk / G::kNDB, db = blk % G::kNDB;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < nsplit; p++) {
+      const f32x4 v = *((const f32x4*)(ws_o + (size_t)(tok * nsplit + p) * HP * D) + blk * 64 + lane);
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[i] += v[i] * wgt[p * HP + hb * 16 + 4 * g + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int h = hb * 16 + 4 * g + i;
+      if (h < H) out[((size_t)tok * H + h) * D + db * 16 + l16] = (__bf16)acc[i];
+    }
+  }
+}
+
+template <int D, int HB>
+static hipError_t launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
+                                int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int nsplit,
+                                void* ws, hipStream_t stream) {
+  const int64_t ntok = B * S;
+  constexpr int HP = HB * 16;
+  float* ws_o = (float*)ws;
+  float* ws_ml = ws_o == nullptr ? nullptr : ws_o + (size_t)ntok * nsplit * HP * D;
+  hipLaunchKernelGGL((sparse_attn_kernel<D, HB>), dim3((unsigned)(ntok * nsplit)), dim3(kThreads), 0, stream,
+                     (const __bf16*)q, (const __bf16*)kv, sink, idx, (__bf16*)out, ws_o, ws_ml, (int)S, (int)H,
+                     (int)T, (int)K, nsplit, scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)ntok), dim3(256), 0, stream, ws_o, ws_ml,
+                     sink, (__bf16*)out, (int)H, nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace sa
+
+// Head blocks (16 heads each) instantiated for H heads.
+extern "C" int sa_internal_head_blocks(int64_t H) {
+  const int hb = (int)((H + 15) / 16);
+  return hb <= 2 ? hb : (hb <= 4 ? 4 : 8);
+}
+
+extern "C" int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx,
+                                         void* out, int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K,
+                                         float scale, int nsplit, void* ws, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int hb = sa_internal_head_blocks(H);
+  hipError_t e;
+#define SA_CASE(DD, HBB) e = sa::launch_sparse<DD, HBB>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, st)
+  if (D == 512) {
+    if (hb == 1) SA_CASE(512, 1); else if (hb == 2) SA_CASE(512, 2); else if (hb == 4) SA_CASE(512, 4); else SA_CASE(512, 8);
+  } else {
+    if (hb == 1) SA_CASE(64, 1); else if (hb == 2) SA_CASE(64, 2); else if (hb == 4) SA_CASE(64, 4); else SA_CASE(64, 8);
+  }
+#undef SA_CASE
+  return e == hipSuccess ? 0 : 1;
+}
