@@ -41,7 +41,21 @@ def parse():
     p.add_argument("--sets", type=int, default=NSETS)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run 5 plain device copies of 256 MiB (reference for the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
 
 
 def sparse_work(inp) -> tuple[float, float]:
@@ -91,6 +105,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import top_sparse_attention_attn_amd as sa
     from top_sparse_attention_attn_amd import workloads as wl
 

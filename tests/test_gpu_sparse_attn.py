@@ -70,11 +70,15 @@ def test_exact_mean_bit_exact():
             idx[b, s, torch.randperm(K, generator=g)[:64]] = rows.to(torch.int32)
             ref[b, s] = kv[b, rows].double().mean(0)
     sink = torch.full((H,), float("-inf"))
-    for splits in (1, 3):
-        out = sa.sparse_attn(q.to(DEV), kv.to(DEV), sink.to(DEV), idx.to(DEV), 1.0, num_splits=splits)
-        torch.cuda.synchronize()
-        got = out.double().cpu()
-        assert torch.equal(got, ref.unsqueeze(2).expand(B, S, H, D)), f"splits={splits}"
+    want = ref.unsqueeze(2).expand(B, S, H, D)
+    out = sa.sparse_attn(q.to(DEV), kv.to(DEV), sink.to(DEV), idx.to(DEV), 1.0, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out.double().cpu(), want)
+    # Split path: each split's normalised partial is rounded to bf16, so the result is exact
+    # only to ~2^-9 relative; a wrong or missing row moves some element by >= 1/64 - that.
+    out = sa.sparse_attn(q.to(DEV), kv.to(DEV), sink.to(DEV), idx.to(DEV), 1.0, num_splits=3)
+    torch.cuda.synchronize()
+    assert (out.double().cpu() - want).abs().max().item() <= 2.0 ** -8
 
 
 def test_single_row_bit_exact():

@@ -49,7 +49,8 @@ size_t sparse_ws_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int nsplit) {
   if (nsplit <= 1) return 0;
   const int64_t hp = (int64_t)sa_internal_head_blocks(H) * 16;
   const int64_t pairs = B * S * nsplit;
-  return (size_t)(pairs * hp * D + pairs * hp * 2) * sizeof(float);
+  // bf16 normalised partial outputs, then one fp32 log-sum-exp per (split, head)
+  return (size_t)(pairs * hp * D) * 2 + (size_t)(pairs * hp) * sizeof(float);
 }
 
 }  // namespace

@@ -13,13 +13,16 @@
 //  * Rows arrive in 32-row tiles through a 4-deep ring of LDS buffers, written by
 //    global_load_lds (16 bytes per lane, one 1 KB row per wave instruction) straight
 //    from memory, two tiles ahead of the tile whose scores are being computed.
-//  * 8 waves, 2 per SIMD, in two roles that run one tile apart:
+//  * 12 waves, 3 per SIMD, in two roles that run one tile apart:
 //      score waves (0-3) keep the queries of two 16-head blocks in registers, compute
-//        S^T = K Q^T for tile t with MFMA 16x16x32 bf16 and the online softmax, write
-//        the bf16 weights P to LDS, then add their share of P V for tile t-1;
-//      value waves (4-7) add the rest of P V for tile t-1.
-//    Every wave owns a slice of the head dimension of the output for all heads; V is
-//    read with the transposing LDS read (ds_read_b64_tr_b16). One barrier per tile.
+//        S^T = K Q^T for tile t with MFMA 16x16x32 bf16 (the K operand of the next
+//        step is read while the current one multiplies) and the online softmax, and
+//        write the bf16 weights P to LDS;
+//      value waves (4-11) gather the rows and add P V for tile t-1, each owning a
+//        slice of the head dimension of the output for all heads; V is read with the
+//        transposing LDS read (ds_read_b64_tr_b16).
+//    One barrier per tile. Score waves hold queries, value waves the accumulators, so
+//    neither runs short of registers for keeping LDS reads in flight.
 //  * Online softmax in base 2 with a lazily moved reference maximum: the output is
 //    rescaled only when a head's maximum grows by more than 2^8 (rare after the first
 //    tile); weights stay <= 2^8, so nothing overflows.
@@ -31,7 +34,8 @@ constexpr int kTile = 32;       // rows per tile
 constexpr int kBufs = 4;        // LDS ring depth (tiles t-1 .. t+2)
 constexpr float kLazy = 8.0f;   // reference-max slack, log2 units
 constexpr int kMaxSplits = 16;
-constexpr int kThreads = 512;
+constexpr int kThreads = 768;   // 4 score waves + 8 value waves
+constexpr int kValueWaves = 8;
 constexpr int kPStride = kTile + 8;  // bf16 elements per P row in LDS (80 bytes)
 
 template <int D>
@@ -41,9 +45,9 @@ struct Geo {
   static constexpr int kDSteps = D / 32;         // QK MFMA steps over the head dimension
   static constexpr int kLanesPerRow = D / 8;     // 16-byte chunks per row
   static constexpr int kNDB = D / 16;            // 16-column output blocks
-  static constexpr int kDBA = kNDB >= 32 ? kNDB / 16 : 1;  // blocks per score wave
-  static constexpr int kDBB = (kNDB - 4 * kDBA) / 4;         // blocks per value wave
-  static_assert(kNDB % 4 == 0 && kDBB >= 0, "head dimension must be a multiple of 64");
+  static constexpr int kDBV = kNDB >= kValueWaves ? kNDB / kValueWaves : 1;  // blocks per value wave
+  static_assert(kNDB % 4 == 0 && (kNDB < kValueWaves || kNDB % kValueWaves == 0),
+                "head dimension must be a multiple of 64");
 };
 
 template <int D, int HB>
@@ -52,7 +56,7 @@ struct Smem {
   __bf16 p[2][HB * 16 * kPStride];
   float alpha[2][HB * 16];
   float fin[HB * 16];
-  unsigned char vmb[kBufs][8];  // per wave: validity of its 4 rows of the tile (one byte each)
+  unsigned char vmb[kBufs][8];  // per value wave: validity of its 4 rows of the tile (one byte each)
   int flag[2][4];
 };
 
@@ -106,19 +110,20 @@ __device__ __forceinline__ void pv_step(Smem<D, HB>& sm, f32x4 (&oacc)[HB][NB > 
 template <int D, int HB, bool SCORE>
 __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
                                           const float* __restrict__ sink, const int* __restrict__ idx,
-                                          __bf16* __restrict__ out, float* __restrict__ ws_o,
-                                          float* __restrict__ ws_ml, int S, int H, int T, int K, int nsplit,
+                                          __bf16* __restrict__ out, __bf16* __restrict__ ws_o,
+                                          float* __restrict__ ws_lse, int S, int H, int T, int K, int nsplit,
                                           float scale_log2) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
-  constexpr int NB = SCORE ? G::kDBA : G::kDBB;  // output column blocks of this wave
+  constexpr int NB = SCORE ? 0 : G::kDBV;  // output column blocks of this wave
   constexpr int NBX = NB > 0 ? NB : 1;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int sw = wave & 3;  // index within the role
-  const int db0 = SCORE ? sw * G::kDBA : 4 * G::kDBA + sw * G::kDBB;
+  const int sw = SCORE ? wave : wave - 4;  // index within the role
+  const int db0 = SCORE ? 0 : sw * G::kDBV;
+  const bool pv_active = !SCORE && db0 < G::kNDB;
 
   const int pair = xcd_local_id(blockIdx.x, gridDim.x);
   const int tok = pair / nsplit, split = pair % nsplit;
@@ -158,9 +163,9 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 #pragma unroll
     for (int db = 0; db < NBX; db++) oacc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- row gather: wave w owns rows 4w .. 4w+3 of every tile
+  // ---- row gather (value waves): value wave v owns rows 4v .. 4v+3 of every tile
   auto load_rows = [&](int tt, int (&rows)[4]) {
-    const int slot0 = (t0 + tt) * kTile + wave * 4;
+    const int slot0 = (t0 + tt) * kTile + sw * 4;
     if (slot0 + 4 <= K) {
 #pragma unroll
       for (int r = 0; r < 4; r++) rows[r] = idx_tok[slot0 + r];
@@ -176,7 +181,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int row = rows[r];
-      unsigned char* dst = &sm.kv[bi][(wave * 4 + r) * G::kRowStride];
+      unsigned char* dst = &sm.kv[bi][(sw * 4 + r) * G::kRowStride];
       if (row >= 0 && row < T) {
         vbits |= 1u << r;
         n++;
@@ -187,7 +192,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         *(uint4*)(dst + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    if (lane == 0) sm.vmb[bi][wave] = (unsigned char)vbits;  // own byte: no clearing needed
+    if (lane == 0) sm.vmb[bi][sw] = (unsigned char)vbits;  // own byte: no clearing needed
     return n;
   };
 
@@ -196,21 +201,26 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   if (threadIdx.x < 8) (&sm.flag[0][0])[threadIdx.x] = 0;
   wait_lgkm0();
   wg_barrier();
-  for (int tt = 0; tt < 2 && tt < ntl; tt++) {
-    int rows[4];
-    load_rows(tt, rows);
-    dma_last = issue(tt, rows);
+  if constexpr (!SCORE) {
+    for (int tt = 0; tt < 2 && tt < ntl; tt++) {
+      int rows[4];
+      load_rows(tt, rows);
+      dma_last = issue(tt, rows);
+    }
+    if (2 < ntl) load_rows(2, rows_next);
   }
-  if (2 < ntl) load_rows(2, rows_next);
 
   for (int tt = 0; tt <= ntl; tt++) {
     // Tile tt's rows have landed once only the younger tile's DMAs may still be pending.
-    wait_vm_lgkm0_dyn(tt + 1 < ntl ? dma_last : 0);
+    if constexpr (SCORE) wait_lgkm0();
+    else wait_vm_lgkm0_dyn(tt + 1 < ntl ? dma_last : 0);
     wg_barrier();  // tile tt and P(tt-1) visible; everyone is done with tile tt-2 and P(tt-2)
     // ---- prefetch tile tt+2 into the buffer freed by tile tt-2
-    if (tt + 2 < ntl) {
-      dma_last = issue(tt + 2, rows_next);
-      if (tt + 3 < ntl) load_rows(tt + 3, rows_next);
+    if constexpr (!SCORE) {
+      if (tt + 2 < ntl) {
+        dma_last = issue(tt + 2, rows_next);
+        if (tt + 3 < ntl) load_rows(tt + 3, rows_next);
+      }
     }
     if constexpr (SCORE) {
       if (tt < ntl) {
@@ -223,30 +233,32 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
           f32x4 sacc[QB][2];
 #pragma unroll
           for (int qi = 0; qi < QB; qi++) sacc[qi][0] = sacc[qi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // Each K operand register is refilled with the next step's operand as soon as its
+          // two MFMAs are issued, so every LDS read overlaps the other block's MFMAs.
+          const unsigned char* kb0 = buf + l16 * G::kRowStride + 16 * g;
+          const unsigned char* kb1 = kb0 + 16 * G::kRowStride;
+          bf16x8 a0 = *(const bf16x8*)kb0, a1 = *(const bf16x8*)kb1;
 #pragma unroll
           for (int s = 0; s < G::kDSteps; s++) {
-            const bf16x8 a0 = *(const bf16x8*)(buf + l16 * G::kRowStride + (32 * s + 8 * g) * 2);
-            const bf16x8 a1 = *(const bf16x8*)(buf + (16 + l16) * G::kRowStride + (32 * s + 8 * g) * 2);
             sacc[0][0] = mfma16x16x32(a0, qreg[0][s], sacc[0][0]);
+            if (QB > 1 && nq > 1) sacc[QB - 1][0] = mfma16x16x32(a0, qreg[QB - 1][s], sacc[QB - 1][0]);
+            if (s + 1 < G::kDSteps) a0 = *(const bf16x8*)(kb0 + 64 * (s + 1));
             sacc[0][1] = mfma16x16x32(a1, qreg[0][s], sacc[0][1]);
-            if (QB > 1 && nq > 1) {
-              sacc[QB - 1][0] = mfma16x16x32(a0, qreg[QB - 1][s], sacc[QB - 1][0]);
-              sacc[QB - 1][1] = mfma16x16x32(a1, qreg[QB - 1][s], sacc[QB - 1][1]);
-            }
+            if (QB > 1 && nq > 1) sacc[QB - 1][1] = mfma16x16x32(a1, qreg[QB - 1][s], sacc[QB - 1][1]);
+            if (s + 1 < G::kDSteps) a1 = *(const bf16x8*)(kb1 + 64 * (s + 1));
           }
 #pragma unroll
           for (int qi = 0; qi < QB; qi++) {
             if (qi >= nq) break;
-            float x[2][4];
+            // logits in log2 units, empty rows masked; computed in place in the accumulators
             float tmax = kNegInf;
 #pragma unroll
             for (int jb = 0; jb < 2; jb++)
 #pragma unroll
               for (int i = 0; i < 4; i++) {
                 const int j = 16 * jb + 4 * g + i;
-                float v = sacc[qi][jb][i] * scale_log2;
-                v = ((vm >> j) & 1u) ? v : kNegInf;
-                x[jb][i] = v;
+                const float v = ((vm >> j) & 1u) ? sacc[qi][jb][i] * scale_log2 : kNegInf;
+                sacc[qi][jb][i] = v;
                 tmax = fmaxf(tmax, v);
               }
             tmax = fmaxf(tmax, xor_shuffle(tmax, 16));
@@ -265,7 +277,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
               bf16x4 pk;
 #pragma unroll
               for (int i = 0; i < 4; i++) {
-                const float p = (mnew > kNegInf) ? exp2_fast(x[jb][i] - mnew) : 0.f;
+                const float p = (mnew > kNegInf) ? exp2_fast(sacc[qi][jb][i] - mnew) : 0.f;
                 const __bf16 pb = (__bf16)p;
                 pk[i] = pb;
                 lsum += (float)pb;
@@ -280,10 +292,12 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         if (lane == 0) sm.flag[par][sw] = __any(any_resc) ? 1 : 0;
       }
     }
-    // ---- P V for the previous tile
-    if (tt >= 1) {
-      const int tp = tt - 1;
-      if (tile_mask(sm, tp % kBufs) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, lane, g, l16);
+    // ---- P V for the previous tile (value waves)
+    if constexpr (!SCORE) {
+      if (tt >= 1 && pv_active) {
+        const int tp = tt - 1;
+        if (tile_mask(sm, tp % kBufs) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, lane, g, l16);
+      }
     }
   }
 
@@ -296,17 +310,20 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     }
   }
 
-  if (nsplit == 1) {
-    // Fold the sink into the normalisation: o = O 2^(m-M) / (l 2^(m-M) + 2^(sink-M)).
-    if constexpr (SCORE) {
+  // Per-head output factor f (score waves own the heads): with no split the sink is folded
+  // in, o = O 2^(m-M) / (l 2^(m-M) + 2^(sink-M)); with splits each split stores its own
+  // normalised output O / l (bf16) and lse = m + log2(l), merged later with the sink.
+  if constexpr (SCORE) {
 #pragma unroll
-      for (int qi = 0; qi < QB; qi++) {
-        if (qi >= nq) break;
-        const int h = (sw + 4 * qi) * 16 + l16;
-        float f = 0.f;
+    for (int qi = 0; qi < QB; qi++) {
+      if (qi >= nq) break;
+      const int h = (sw + 4 * qi) * 16 + l16;
+      const float m = m_ref[qi];
+      const float l = l_part[qi];
+      float f = 0.f;
+      if (nsplit == 1) {
         if (h < H) {
           const float sk = sink[h];
-          const float m = m_ref[qi];
           if (__builtin_isnan(sk)) {
             f = __builtin_nanf("");
           } else if (sk == __builtin_huge_valf()) {
@@ -316,17 +333,23 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
             const float M = fmaxf(m, s2);
             if (M > kNegInf) {
               const float c = (m > kNegInf) ? exp2_fast(m - M) : 0.f;
-              const float L = l_part[qi] * c + ((s2 > kNegInf) ? exp2_fast(s2 - M) : 0.f);
+              const float L = l * c + ((s2 > kNegInf) ? exp2_fast(s2 - M) : 0.f);
               f = c / L;
             }
           }
         }
-        if (g == 0) sm.fin[h] = f;
+      } else {
+        f = (m > kNegInf && l > 0.f) ? 1.f / l : 0.f;
+        if (g == 0) ws_lse[(size_t)pair * HP + h] = (m > kNegInf && l > 0.f) ? m + __builtin_log2f(l) : kNegInf;
       }
+      if (g == 0) sm.fin[h] = f;
     }
-    wait_lgkm0();
-    wg_barrier();
-    if constexpr (NB > 0) {
+  }
+  wait_lgkm0();
+  wg_barrier();
+  if constexpr (NB > 0) {
+    if (!pv_active) return;
+    if (nsplit == 1) {
 #pragma unroll
       for (int hb = 0; hb < HB; hb++)
 #pragma unroll
@@ -338,25 +361,21 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 #pragma unroll
           for (int db = 0; db < NB; db++) orow[db * 16] = (__bf16)(oacc[hb][db][i] * f);
         }
-    }
-  } else {
-    // Partial results for the combine kernel: block (hb, db) of MFMA accumulators, 16 bytes
-    // per lane, at ws_o[pair][hb][db][lane].
-    if constexpr (NB > 0) {
-      f32x4* wo = (f32x4*)(ws_o + (size_t)pair * HP * D) + lane;
+    } else {
+      // Split partial: block (hb, db) of normalised accumulators as bf16, 8 bytes per lane,
+      // at ws_o[pair][hb][db][lane][0..3].
+      bf16x4* wo = (bf16x4*)(ws_o + (size_t)pair * HP * D) + lane;
 #pragma unroll
-      for (int hb = 0; hb < HB; hb++)
+      for (int hb = 0; hb < HB; hb++) {
+        float f[4];
 #pragma unroll
-        for (int db = 0; db < NB; db++) wo[(hb * G::kNDB + db0 + db) * 64] = oacc[hb][db];
-    }
-    if constexpr (SCORE) {
+        for (int i = 0; i < 4; i++) f[i] = sm.fin[hb * 16 + 4 * g + i];
 #pragma unroll
-      for (int qi = 0; qi < QB; qi++) {
-        if (qi >= nq) break;
-        const int h = (sw + 4 * qi) * 16 + l16;
-        if (g == 0) {
-          ws_ml[((size_t)pair * HP + h) * 2 + 0] = m_ref[qi];
-          ws_ml[((size_t)pair * HP + h) * 2 + 1] = l_part[qi];
+        for (int db = 0; db < NB; db++) {
+          bf16x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; i++) v[i] = (__bf16)(oacc[hb][db][i] * f[i]);
+          wo[(hb * G::kNDB + db0 + db) * 64] = v;
         }
       }
     }
@@ -366,55 +385,56 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 template <int D, int HB>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv, const float* __restrict__ sink,
-    const int* __restrict__ idx, __bf16* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const int* __restrict__ idx, __bf16* __restrict__ out, __bf16* __restrict__ ws_o, float* __restrict__ ws_lse,
     int S, int H, int T, int K, int nsplit, float scale_log2) {
   __shared__ __attribute__((aligned(16))) Smem<D, HB> sm;
-  if (threadIdx.x < 256)
-    run_split<D, HB, true>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, scale_log2);
+  if (threadIdx.x < 256)  // waves 0-3
+    run_split<D, HB, true>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, scale_log2);
   else
-    run_split<D, HB, false>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, scale_log2);
+    run_split<D, HB, false>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, scale_log2);
 }
 
-// Merge the split partials of one token (log-sum-exp in base 2) and add the sink once.
+// Merge the split partials of one (token, 16-head block) and add the sink once:
+// o = sum_p 2^(lse_p - M) o_p / (sum_p 2^(lse_p - M) + 2^(sink - M)), M the largest term.
+// Grid: tokens x head blocks; each wave merges 512-byte blocks of partial outputs.
 template <int D, int HB>
-__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const float* __restrict__ ws_o,
-                                                                   const float* __restrict__ ws_ml,
+__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* __restrict__ ws_o,
+                                                                   const float* __restrict__ ws_lse,
                                                                    const float* __restrict__ sink,
                                                                    __bf16* __restrict__ out, int H, int nsplit) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
-  __shared__ float wgt[kMaxSplits * HP];
-  const int tok = blockIdx.x;
-  for (int h = threadIdx.x; h < HP; h += blockDim.x) {
+  __shared__ float wgt[kMaxSplits * 16];
+  const int tok = blockIdx.x / HB, hb = blockIdx.x % HB;
+  if (threadIdx.x < 16) {
+    const int h = hb * 16 + threadIdx.x;
     const float sk = h < H ? sink[h] : kNegInf;
     const float s2 = sk * kLog2e;
     float M = s2;
-    for (int p = 0; p < nsplit; p++) M = fmaxf(M, ws_ml[(((size_t)tok * nsplit + p) * HP + h) * 2]);
+    for (int p = 0; p < nsplit; p++) M = fmaxf(M, ws_lse[((size_t)tok * nsplit + p) * HP + h]);
     float L = (s2 > kNegInf && M > kNegInf) ? exp2_fast(s2 - M) : 0.f;
     for (int p = 0; p < nsplit; p++) {
-      const float m = ws_ml[(((size_t)tok * nsplit + p) * HP + h) * 2];
-      const float l = ws_ml[(((size_t)tok * nsplit + p) * HP + h) * 2 + 1];
-      L += (m > kNegInf) ? l * exp2_fast(m - M) : 0.f;
+      const float e = ws_lse[((size_t)tok * nsplit + p) * HP + h];
+      L += (e > kNegInf) ? exp2_fast(e - M) : 0.f;
     }
     for (int p = 0; p < nsplit; p++) {
-      const float m = ws_ml[(((size_t)tok * nsplit + p) * HP + h) * 2];
-      float w = (m > kNegInf && M > kNegInf) ? exp2_fast(m - M) / L : 0.f;
+      const float e = ws_lse[((size_t)tok * nsplit + p) * HP + h];
+      float w = (e > kNegInf && M > kNegInf) ? exp2_fast(e - M) / L : 0.f;
       if (__builtin_isnan(sk)) w = __builtin_nanf("");
       else if (sk == __builtin_huge_valf()) w = 0.f;
-      wgt[p * HP + h] = w;
+      wgt[p * 16 + threadIdx.x] = w;
     }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  constexpr int NBLK = HB * G::kNDB;  // (hb, db) blocks of 64 lanes x 4 floats
-  for (int blk = threadIdx.x >> 6; blk < NBLK; blk += blockDim.x >> 6) {
-    const int hb = blk / G::kNDB, db = blk % G::kNDB;
+  for (int db = wave; db < G::kNDB; db += 4) {
+    const int blk = hb * G::kNDB + db;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < nsplit; p++) {
-      const f32x4 v = *((const f32x4*)(ws_o + (size_t)(tok * nsplit + p) * HP * D) + blk * 64 + lane);
+      const bf16x4 v = *((const bf16x4*)(ws_o + (size_t)(tok * nsplit + p) * HP * D) + blk * 64 + lane);
 #pragma unroll
-      for (int i = 0; i < 4; i++) acc[i] += v[i] * wgt[p * HP + hb * 16 + 4 * g + i];
+      for (int i = 0; i < 4; i++) acc[i] += (float)v[i] * wgt[p * 16 + 4 * g + i];
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -430,14 +450,14 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
                                 void* ws, hipStream_t stream) {
   const int64_t ntok = B * S;
   constexpr int HP = HB * 16;
-  float* ws_o = (float*)ws;
-  float* ws_ml = ws_o == nullptr ? nullptr : ws_o + (size_t)ntok * nsplit * HP * D;
+  __bf16* ws_o = (__bf16*)ws;
+  float* ws_lse = ws_o == nullptr ? nullptr : (float*)(ws_o + (size_t)ntok * nsplit * HP * D);
   hipLaunchKernelGGL((sparse_attn_kernel<D, HB>), dim3((unsigned)(ntok * nsplit)), dim3(kThreads), 0, stream,
-                     (const __bf16*)q, (const __bf16*)kv, sink, idx, (__bf16*)out, ws_o, ws_ml, (int)S, (int)H,
+                     (const __bf16*)q, (const __bf16*)kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H,
                      (int)T, (int)K, nsplit, scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)ntok), dim3(256), 0, stream, ws_o, ws_ml,
+  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)(ntok * HB)), dim3(256), 0, stream, ws_o, ws_lse,
                      sink, (__bf16*)out, (int)H, nsplit);
   return hipGetLastError();
 }
