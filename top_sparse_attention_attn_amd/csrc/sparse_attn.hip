@@ -40,7 +40,10 @@ constexpr int kPStride = kTile + 8;  // bf16 elements per P row in LDS (80 bytes
 
 template <int D>
 struct Geo {
-  static constexpr int kRowStride = D * 2 + 16;  // padded LDS row: spreads rows over banks
+  // Padded LDS row (D*2 + 32 bytes, 8 banks of skew per row): the K operand reads (16 bytes of
+  // 16 rows) and the transposed V reads (8 bytes of 4 rows per 16 lanes, rows 4g..4g+3) are
+  // then free of bank conflicts on the 64-bank LDS.
+  static constexpr int kRowStride = D * 2 + 32;
   static constexpr int kBufBytes = kTile * kRowStride;
   static constexpr int kDSteps = D / 32;         // QK MFMA steps over the head dimension
   static constexpr int kLanesPerRow = D / 8;     // 16-byte chunks per row
@@ -54,6 +57,11 @@ template <int D, int HB>
 struct Smem {
   unsigned char kv[kBufs][Geo<D>::kBufBytes];
   __bf16 p[2][HB * 16 * kPStride];
+  // per-head softmax state, contiguous in this order (the score waves address all of it
+  // from one base): reference maximum (log2 units), running weight sum, and the rescale
+  // factor of the last two tiles for the value waves
+  float mref[HB * 16];
+  float lsum[HB * 16];
   float alpha[2][HB * 16];
   float fin[HB * 16];
   unsigned char vmb[kBufs][8];  // per value wave: validity of its 4 rows of the tile (one byte each)
@@ -89,14 +97,15 @@ __device__ __forceinline__ void pv_step(Smem<D, HB>& sm, f32x4 (&oacc)[HB][NB > 
         }
     }
     // V operands of this wave's column blocks (transposed reads), then one P operand per
-    // head block: keeps at most one P operand live.
+    // head block: keeps at most one P operand live. The MFMA's k index 8g+i stands for tile
+    // row 4g+i (i < 4) or 16+4g+i-4 (i >= 4); P is stored in LDS in the same order.
     const int r4 = (lane >> 2) & 3, c4 = lane & 3;
-    const unsigned char* vbase = &sm.kv[bi][(8 * g + r4) * G::kRowStride + (db0 * 16 + 4 * c4) * 2];
+    const unsigned char* vbase = &sm.kv[bi][(4 * g + r4) * G::kRowStride + (db0 * 16 + 4 * c4) * 2];
     bf16x8 bv[NB];
 #pragma unroll
     for (int db = 0; db < NB; db++) {
       const unsigned char* p0 = vbase + db * 32;
-      bv[db] = concat_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * G::kRowStride));
+      bv[db] = concat_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 16 * G::kRowStride));
     }
 #pragma unroll
     for (int hb = 0; hb < HB; hb++) {
@@ -117,6 +126,10 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   constexpr int HP = HB * 16;
   constexpr int NB = SCORE ? 0 : G::kDBV;  // output column blocks of this wave
   constexpr int NBX = NB > 0 ? NB : 1;
+  using SM = Smem<D, HB>;
+  static_assert(offsetof(SM, lsum) == offsetof(SM, mref) + HP * 4 &&
+                    offsetof(SM, alpha) == offsetof(SM, mref) + 2 * HP * 4,
+                "per-head state must be contiguous");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -138,7 +151,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   constexpr int QB = SCORE ? (HB > 4 ? 2 : 1) : 1;
   const int nq = SCORE ? ((sw + 4 < HB) ? 2 : ((sw < HB) ? 1 : 0)) : 0;
   bf16x8 qreg[QB][SCORE ? G::kDSteps : 1];
-  float m_ref[QB], l_part[QB];
+  float l_fin[QB];
   if constexpr (SCORE) {
 #pragma unroll
     for (int qi = 0; qi < QB; qi++) {
@@ -149,8 +162,10 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         if (qi < nq && h < H) v = *(const bf16x8*)(q + ((size_t)tok * H + h) * D + 32 * s + 8 * g);
         qreg[qi][s] = v;
       }
-      m_ref[qi] = kNegInf;
-      l_part[qi] = 0.f;
+      if (g == 0 && qi < nq) {
+        sm.mref[(sw + 4 * qi) * 16 + l16] = kNegInf;
+        sm.lsum[(sw + 4 * qi) * 16 + l16] = 0.f;
+      }
     }
     // Let the query loads land before any row DMA is issued, so that no wait for them is
     // left inside the tile loop (it would also drain the DMA queue).
@@ -198,9 +213,8 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 
   int rows_next[4];
   int dma_last = 0;  // DMA count of the most recently issued tile
-  if (threadIdx.x < 8) (&sm.flag[0][0])[threadIdx.x] = 0;
-  wait_lgkm0();
-  wg_barrier();
+  // Value waves start the gather of tiles 0 and 1 at once: it overlaps the query loads of the
+  // score waves (each wave waits only on its own memory counter).
   if constexpr (!SCORE) {
     for (int tt = 0; tt < 2 && tt < ntl; tt++) {
       int rows[4];
@@ -208,6 +222,10 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
       dma_last = issue(tt, rows);
     }
     if (2 < ntl) load_rows(2, rows_next);
+  } else {
+    // Score waves win MFMA issue arbitration over the value waves of their SIMD, so the
+    // scores of a tile are ready early and the softmax runs beside the value waves' PV.
+    __builtin_amdgcn_s_setprio(2);
   }
 
   for (int tt = 0; tt <= ntl; tt++) {
@@ -217,75 +235,119 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     wg_barrier();  // tile tt and P(tt-1) visible; everyone is done with tile tt-2 and P(tt-2)
     // ---- prefetch tile tt+2 into the buffer freed by tile tt-2
     if constexpr (!SCORE) {
-      if (tt + 2 < ntl) {
-        dma_last = issue(tt + 2, rows_next);
-        if (tt + 3 < ntl) load_rows(tt + 3, rows_next);
+      if (tt + 2 < ntl) dma_last = issue(tt + 2, rows_next);
+    }
+    // ---- scores of tile tt (score waves)
+    f32x4 sacc[QB][2];
+    unsigned vm = 0u;
+    if constexpr (SCORE) {
+      if (tt < ntl) vm = tile_mask(sm, tt % kBufs);
+      if (vm != 0u && nq > 0) {
+        const unsigned char* buf = sm.kv[tt % kBufs];
+#pragma unroll
+        for (int qi = 0; qi < QB; qi++) sacc[qi][0] = sacc[qi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // K operands in the order k = 2s + jb (step s over the head dimension, 16-row block jb),
+        // each feeding the MFMAs of both head blocks; four registers rotate so every LDS read
+        // is issued four operands (eight MFMAs) ahead of its use. The schedule groups keep
+        // the compiler from collapsing the rotation.
+        const unsigned char* kb = buf + l16 * G::kRowStride + 16 * g;
+        constexpr int NK = 2 * G::kDSteps;
+        constexpr int KR = NK < 4 ? NK : 4;
+        auto kop = [&](int k) { return *(const bf16x8*)(kb + (k & 1) * 16 * G::kRowStride + 64 * (k >> 1)); };
+        bf16x8 ka[KR];
+#pragma unroll
+        for (int k = 0; k < KR; k++) ka[k] = kop(k);
+        __builtin_amdgcn_sched_group_barrier(0x100, KR, 0);
+#pragma unroll
+        for (int k = 0; k < NK; k++) {
+          const int st = k >> 1, jb = k & 1;
+          sacc[0][jb] = mfma16x16x32(ka[k % KR], qreg[0][st], sacc[0][jb]);
+          if (QB > 1) sacc[QB - 1][jb] = mfma16x16x32(ka[k % KR], qreg[QB - 1][st], sacc[QB - 1][jb]);
+          __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+          if (k + KR < NK) {
+            ka[k % KR] = kop(k + KR);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+#ifdef SA_PHASE_BARRIER
+    // The value waves start PV only once the K reads of the scores are issued, so PV's LDS
+    // traffic and MFMAs overlap the softmax instead of competing with QK.
+    wg_barrier();
+#endif
+    // ---- online softmax of tile tt (score waves)
     if constexpr (SCORE) {
       if (tt < ntl) {
-        const int bi = tt % kBufs;
         const int par = tt & 1;
-        const unsigned vm = tile_mask(sm, bi);
         bool any_resc = false;
         if (vm != 0u && nq > 0) {
-          const unsigned char* buf = sm.kv[bi];
-          f32x4 sacc[QB][2];
-#pragma unroll
-          for (int qi = 0; qi < QB; qi++) sacc[qi][0] = sacc[qi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-          // Each K operand register is refilled with the next step's operand as soon as its
-          // two MFMAs are issued, so every LDS read overlaps the other block's MFMAs.
-          const unsigned char* kb0 = buf + l16 * G::kRowStride + 16 * g;
-          const unsigned char* kb1 = kb0 + 16 * G::kRowStride;
-          bf16x8 a0 = *(const bf16x8*)kb0, a1 = *(const bf16x8*)kb1;
-#pragma unroll
-          for (int s = 0; s < G::kDSteps; s++) {
-            sacc[0][0] = mfma16x16x32(a0, qreg[0][s], sacc[0][0]);
-            if (QB > 1 && nq > 1) sacc[QB - 1][0] = mfma16x16x32(a0, qreg[QB - 1][s], sacc[QB - 1][0]);
-            if (s + 1 < G::kDSteps) a0 = *(const bf16x8*)(kb0 + 64 * (s + 1));
-            sacc[0][1] = mfma16x16x32(a1, qreg[0][s], sacc[0][1]);
-            if (QB > 1 && nq > 1) sacc[QB - 1][1] = mfma16x16x32(a1, qreg[QB - 1][s], sacc[QB - 1][1]);
-            if (s + 1 < G::kDSteps) a1 = *(const bf16x8*)(kb1 + 64 * (s + 1));
-          }
+          // Lane-dependent LDS offsets are rebuilt here from the lane id (kept opaque so the
+          // compiler cannot carry them, or spill them, across the QK loop); every access
+          // below is one of these two offsets plus a constant.
+          unsigned ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+          asm volatile("" : "+v"(ln));
+          const int lg = (int)(ln >> 4), ll = (int)(ln & 15u);
+          const int off_h = (sw * 16 + ll) * 4;                       // per-head state, bytes
+          const int off_p = (sw * 16 + ll) * (kPStride * 2) + 16 * lg;  // P row, bytes
+          unsigned char* const hst = (unsigned char*)&sm.mref[0] + off_h;
+          unsigned char* const pst = (unsigned char*)&sm.p[par][0] + off_p;
+          constexpr int kHB = HP * 4;  // bytes of one per-head array
+          // softmax state of this lane's heads, read first so the LDS latency overlaps the
+          // masking and maximum below
+          float mst[QB], lst[QB];
 #pragma unroll
           for (int qi = 0; qi < QB; qi++) {
-            if (qi >= nq) break;
+            mst[qi] = *(const float*)(hst + qi * 256);
+            lst[qi] = *(const float*)(hst + kHB + qi * 256);
+          }
+          // validity of this lane's rows 4g+i and 16+4g+i: bits i and 16+i of vg (one shift per
+          // tile, immediate masks after it)
+          const unsigned vg = vm >> (4 * lg);
+#pragma unroll
+          for (int qi = 0; qi < QB; qi++) {
             // logits in log2 units, empty rows masked; computed in place in the accumulators
             float tmax = kNegInf;
 #pragma unroll
             for (int jb = 0; jb < 2; jb++)
 #pragma unroll
               for (int i = 0; i < 4; i++) {
-                const int j = 16 * jb + 4 * g + i;
-                const float v = ((vm >> j) & 1u) ? sacc[qi][jb][i] * scale_log2 : kNegInf;
+                const float v = (vg & (1u << (16 * jb + i))) ? sacc[qi][jb][i] * scale_log2 : kNegInf;
                 sacc[qi][jb][i] = v;
                 tmax = fmaxf(tmax, v);
               }
-            tmax = fmaxf(tmax, xor_shuffle(tmax, 16));
-            tmax = fmaxf(tmax, xor_shuffle(tmax, 32));
-            const float mold = m_ref[qi];
+            tmax = max4_x16_x32(tmax);
+            const float mold = mst[qi];
             const bool move = tmax > mold + kLazy;  // also true for the first finite maximum
             const float mnew = move ? tmax : mold;
-            const float alpha = move ? exp2_fast(mold - mnew) : 1.f;
+            const float alpha = move ? exp2_fast(mold - mnew) : 1.f;  // 0 when mold = -inf
             const bool resc = move && (mold > kNegInf);
             any_resc |= resc;
-            m_ref[qi] = mnew;
-            float lsum = l_part[qi] * alpha;
-            const int h = (sw + 4 * qi) * 16 + l16;
+            const float msub = (mnew > kNegInf) ? mnew : 0.f;  // no finite logit yet: all weights 0
+            float lsum = 0.f;
+            // this lane's weights for rows 4g+i and 16+4g+i go to P columns 8g .. 8g+7
+            bf16x2 pk[4];
 #pragma unroll
             for (int jb = 0; jb < 2; jb++) {
-              bf16x4 pk;
+              float pw[4];
 #pragma unroll
               for (int i = 0; i < 4; i++) {
-                const float p = (mnew > kNegInf) ? exp2_fast(sacc[qi][jb][i] - mnew) : 0.f;
-                const __bf16 pb = (__bf16)p;
-                pk[i] = pb;
-                lsum += (float)pb;
+                pw[i] = exp2_fast(sacc[qi][jb][i] - msub);
+                lsum += pw[i];
               }
-              *(bf16x4*)(&sm.p[par][h * kPStride + 16 * jb + 4 * g]) = pk;
+              pk[2 * jb] = __builtin_convertvector((f32x2){pw[0], pw[1]}, bf16x2);
+              pk[2 * jb + 1] = __builtin_convertvector((f32x2){pw[2], pw[3]}, bf16x2);
             }
-            l_part[qi] = lsum;
-            if (g == 0) sm.alpha[par][h] = resc ? alpha : 1.f;
+            *(bf16x8*)(pst + qi * (64 * kPStride * 2)) =
+                bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
+            // the row sum uses the fp32 weights; the MFMA operand is their bf16 rounding
+            lsum = sum4_x16_x32(lsum);
+            if (lg == 0) {
+              *(float*)(hst + qi * 256) = mnew;
+              *(float*)(hst + kHB + qi * 256) = lst[qi] * alpha + lsum;
+              *(float*)(hst + (2 + par) * kHB + qi * 256) = resc ? alpha : 1.f;
+            }
           }
         }
         // Every score wave publishes its own rescale flag for this tile (no shared writes).
@@ -298,16 +360,17 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         const int tp = tt - 1;
         if (tile_mask(sm, tp % kBufs) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, lane, g, l16);
       }
+      // Index loads of tile tt+3 go out after PV: scalar loads share the LDS wait counter, so
+      // issued earlier they would hold up every LDS wait of PV. Their latency overlaps this
+      // wave's wait at the next barrier.
+      if (tt + 3 < ntl) load_rows(tt + 3, rows_next);
     }
   }
 
   // ---- per-head totals (score waves): sum the partial row sums over the 4 lane groups
   if constexpr (SCORE) {
 #pragma unroll
-    for (int qi = 0; qi < QB; qi++) {
-      l_part[qi] += xor_shuffle(l_part[qi], 16);
-      l_part[qi] += xor_shuffle(l_part[qi], 32);
-    }
+    for (int qi = 0; qi < QB; qi++) l_fin[qi] = sm.lsum[(sw + 4 * qi) * 16 + l16];
   }
 
   // Per-head output factor f (score waves own the heads): with no split the sink is folded
@@ -318,8 +381,8 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     for (int qi = 0; qi < QB; qi++) {
       if (qi >= nq) break;
       const int h = (sw + 4 * qi) * 16 + l16;
-      const float m = m_ref[qi];
-      const float l = l_part[qi];
+      const float m = sm.mref[h];
+      const float l = l_fin[qi];
       float f = 0.f;
       if (nsplit == 1) {
         if (h < H) {
@@ -396,7 +459,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 
 // Merge the split partials of one (token, 16-head block) and add the sink once:
 // o = sum_p 2^(lse_p - M) o_p / (sum_p 2^(lse_p - M) + 2^(sink - M)), M the largest term.
-// Grid: tokens x head blocks; each wave merges 512-byte blocks of partial outputs.
+// Grid: tokens x head blocks (mapped so a token's blocks run on the XCD that wrote its
+// partials). The block's partials are 16-byte chunks of the MFMA output layout
+// [d block][lane][4 heads]; every thread issues all its chunk loads of a group of up to four
+// splits before it waits, then the merged block is staged in LDS and stored row by row.
 template <int D, int HB>
 __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* __restrict__ ws_o,
                                                                    const float* __restrict__ ws_lse,
@@ -404,43 +470,101 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* 
                                                                    __bf16* __restrict__ out, int H, int nsplit) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
+  constexpr int kChunks = G::kNDB * 64 * 8 / 16;       // 16-byte chunks of one partial block
+  constexpr int kPerThread = (kChunks + 255) / 256;    // chunks per thread
+  constexpr int kOutStride = D + 8;                    // bf16 per staged output row
   __shared__ float wgt[kMaxSplits * 16];
-  const int tok = blockIdx.x / HB, hb = blockIdx.x % HB;
-  if (threadIdx.x < 16) {
-    const int h = hb * 16 + threadIdx.x;
-    const float sk = h < H ? sink[h] : kNegInf;
-    const float s2 = sk * kLog2e;
-    float M = s2;
-    for (int p = 0; p < nsplit; p++) M = fmaxf(M, ws_lse[((size_t)tok * nsplit + p) * HP + h]);
-    float L = (s2 > kNegInf && M > kNegInf) ? exp2_fast(s2 - M) : 0.f;
-    for (int p = 0; p < nsplit; p++) {
-      const float e = ws_lse[((size_t)tok * nsplit + p) * HP + h];
-      L += (e > kNegInf) ? exp2_fast(e - M) : 0.f;
+  __shared__ __attribute__((aligned(16))) __bf16 stage[16 * kOutStride];
+  const int blk = xcd_local_id(blockIdx.x, gridDim.x);
+  const int tok = blk / HB, hb = blk % HB;
+  const int t = threadIdx.x;
+
+  // chunk c of a block holds lanes 2(c%32), 2(c%32)+1 of d block c/32: heads 4*(lane/16)+i,
+  // columns (c/32)*16 + lane%16 (+1 for the odd lane)
+  f32x4 acc[kPerThread][2];
+#pragma unroll
+  for (int j = 0; j < kPerThread; j++) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // weights: thread t < 16 owns head hb*16+t; its log-sum-exp values are loaded in one round
+  float lse[kMaxSplits];
+  float sk = kNegInf;
+  if (t < 16) {
+    const int h = hb * 16 + t;
+    sk = h < H ? sink[h] : kNegInf;
+#pragma unroll
+    for (int p = 0; p < kMaxSplits; p++) lse[p] = p < nsplit ? ws_lse[((size_t)tok * nsplit + p) * HP + h] : kNegInf;
+  }
+  for (int p0 = 0; p0 < nsplit; p0 += 4) {
+    const int np = nsplit - p0 < 4 ? nsplit - p0 : 4;
+    uint4 v[4][kPerThread];
+#pragma unroll
+    for (int pp = 0; pp < 4; pp++) {
+      if (pp < np) {
+        const uint4* src = (const uint4*)(ws_o + ((size_t)(tok * nsplit + p0 + pp) * HP + hb * 16) * D);
+#pragma unroll
+        for (int j = 0; j < kPerThread; j++) {
+          const int c = t + 256 * j;
+          if (c < kChunks) v[pp][j] = src[c];
+        }
+      }
     }
-    for (int p = 0; p < nsplit; p++) {
-      const float e = ws_lse[((size_t)tok * nsplit + p) * HP + h];
-      float w = (e > kNegInf && M > kNegInf) ? exp2_fast(e - M) / L : 0.f;
-      if (__builtin_isnan(sk)) w = __builtin_nanf("");
-      else if (sk == __builtin_huge_valf()) w = 0.f;
-      wgt[p * 16 + threadIdx.x] = w;
+    if (p0 == 0) {
+      if (t < 16) {
+        const float s2 = sk * kLog2e;
+        float M = s2;
+#pragma unroll
+        for (int p = 0; p < kMaxSplits; p++) M = fmaxf(M, lse[p]);
+        float L = (s2 > kNegInf && M > kNegInf) ? exp2_fast(s2 - M) : 0.f;
+#pragma unroll
+        for (int p = 0; p < kMaxSplits; p++) L += (lse[p] > kNegInf) ? exp2_fast(lse[p] - M) : 0.f;
+#pragma unroll
+        for (int p = 0; p < kMaxSplits; p++) {
+          if (p >= nsplit) break;
+          float w = (lse[p] > kNegInf && M > kNegInf) ? exp2_fast(lse[p] - M) / L : 0.f;
+          if (__builtin_isnan(sk)) w = __builtin_nanf("");
+          else if (sk == __builtin_huge_valf()) w = 0.f;
+          wgt[p * 16 + t] = w;
+        }
+      }
+      __syncthreads();  // weights ready; the chunk loads above are already in flight
+    }
+#pragma unroll
+    for (int pp = 0; pp < 4; pp++) {
+      if (pp < np) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; j++) {
+          const int c = t + 256 * j;
+          if (c >= kChunks) continue;
+          const int hq = 4 * ((2 * (c & 31)) >> 4);
+          const bf16x8 x = __builtin_bit_cast(bf16x8, v[pp][j]);
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float w = wgt[(p0 + pp) * 16 + hq + i];
+            acc[j][0][i] += (float)x[i] * w;
+            acc[j][1][i] += (float)x[4 + i] * w;
+          }
+        }
+      }
+    }
+  }
+  // stage the merged 16 x D block as bf16 rows, then store each row with 16-byte writes
+#pragma unroll
+  for (int j = 0; j < kPerThread; j++) {
+    const int c = t + 256 * j;
+    if (c >= kChunks) continue;
+    const int lane0 = 2 * (c & 31), col = (c >> 5) * 16 + (lane0 & 15), hq = 4 * (lane0 >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const bf16x2 pr = __builtin_convertvector((f32x2){acc[j][0][i], acc[j][1][i]}, bf16x2);
+      *(bf16x2*)(&stage[(hq + i) * kOutStride + col]) = pr;
     }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  for (int db = wave; db < G::kNDB; db += 4) {
-    const int blk = hb * G::kNDB + db;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < nsplit; p++) {
-      const bf16x4 v = *((const bf16x4*)(ws_o + (size_t)(tok * nsplit + p) * HP * D) + blk * 64 + lane);
-#pragma unroll
-      for (int i = 0; i < 4; i++) acc[i] += (float)v[i] * wgt[p * 16 + 4 * g + i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int h = hb * 16 + 4 * g + i;
-      if (h < H) out[((size_t)tok * H + h) * D + db * 16 + l16] = (__bf16)acc[i];
-    }
+  constexpr int kRowChunks = D / 8;  // 16-byte chunks per output row
+  for (int c = t; c < 16 * kRowChunks; c += 256) {
+    const int r = c / kRowChunks, k = c % kRowChunks;
+    const int h = hb * 16 + r;
+    if (h < H) *(uint4*)(out + ((size_t)tok * H + h) * D + 8 * k) = *(const uint4*)(&stage[r * kOutStride + 8 * k]);
   }
 }
 
