@@ -121,8 +121,7 @@ def main():
         sets = [wl.sparse_inputs(cfg, 2001 + i, dev) for i in range(nsets)]
         out = torch.empty_like(sets[0]["q"])
         ws_bytes = sa.sparse_attn_workspace_bytes(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)
-        ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
-        ws = ws[(-ws.data_ptr()) % 256:]
+        ws = sa.new_workspace(ws_bytes, dev)
 
         def step(i):
             x = sets[i % nsets]

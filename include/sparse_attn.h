@@ -86,8 +86,10 @@ int sparse_attn_num_splits(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K
  * scale      the softmax scale (the pages use D^-0.5)
  * num_splits 0 = library choice, else 1..64 (clamped to K's tile count)
  * workspace  device, >= sparse_attn_workspace_bytes(...) bytes, 256-byte
- *            aligned; may be NULL when that size is 0. Contents on entry do
- *            not matter; contents on return are unspecified.
+ *            aligned; may be NULL when that size is 0. Scratch for the split
+ *            partials: contents on entry do not matter, on return they are
+ *            unspecified. Calls that may run at the same time need separate
+ *            workspaces.
  * Supported: D in {64, 512}; 1 <= H <= 128. q, kv, out 16-byte aligned.
  */
 int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,

@@ -199,8 +199,7 @@ def test_graph_replay_tracks_new_indices(oracle_impl):
     """Capture once, replay with new index lists (grid depends only on shapes)."""
     inp = _custom(4, 1, 128, 512, 600, 320, seed=21)
     out = torch.empty_like(inp["q"])
-    ws = torch.empty(sa.sparse_attn_workspace_bytes(4, 1, 128, 512, 320) + 256, dtype=torch.uint8, device=DEV)
-    ws = ws[(-ws.data_ptr()) % 256:]
+    ws = sa.new_workspace(sa.sparse_attn_workspace_bytes(4, 1, 128, 512, 320), DEV)
     _run(inp, out=out, workspace=ws)  # warm up outside the graph
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -214,3 +213,34 @@ def test_graph_replay_tracks_new_indices(oracle_impl):
         torch.cuda.synchronize()
         ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
         assert_close(to64(out).reshape(ref.shape), ref, f"replay {rep}")
+
+
+# More tokens and splits: every split's partial goes through the merge kernel.
+@pytest.mark.parametrize("D,H,B,S,splits", [(512, 128, 16, 1, 4), (512, 128, 8, 2, 2), (512, 16, 4, 2, 8),
+                                            (64, 64, 16, 1, 4), (512, 40, 8, 1, 16), (512, 128, 64, 1, 4)])
+def test_split_merge_shapes(oracle_impl, D, H, B, S, splits):
+    inp = _custom(B, S, H, D, 700, 640, seed=31 + H + splits)
+    ws = sa.new_workspace(sa.sparse_attn_workspace_bytes(B, S, H, D, 640, splits), DEV)
+    out = _run(inp, num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    tokens = np.arange(0, B * S, max(1, B * S // 6))
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"], tokens)
+    got = to64(out.reshape(B * S, H, D)[torch.as_tensor(tokens, device=DEV)])
+    assert_close(got, ref, f"merge D={D} H={H} B={B} S={S} splits={splits}")
+
+
+def test_split_merge_special_cases():
+    """All-invalid rows, a single row in the last split, sink specials (16 tokens, 4 splits)."""
+    inp = _custom(16, 1, 128, 512, 300, 256, seed=41)
+    inp["topk_idxs"][0].fill_(-1)                  # token 0: nothing valid
+    inp["topk_idxs"][1].fill_(-1)
+    inp["topk_idxs"][1, 0, 200] = 17               # token 1: one row in the last split only
+    inp["attn_sink"][0] = float("inf")
+    inp["attn_sink"][1] = float("nan")
+    inp["attn_sink"][2:].fill_(float("-inf"))
+    out = _run(inp, num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[0, :, 2:]).item() == 0
+    assert torch.equal(out[1, 0, 2:], inp["kv"][1, 17].expand(126, 512))
+    assert torch.count_nonzero(out[:, :, 0]).item() == 0
+    assert torch.isnan(out[:, :, 1]).all()

@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     SparseAttnError,
     library_path,
     masked_attn,
+    new_workspace,
     sparse_attn,
     sparse_attn_num_splits,
     sparse_attn_workspace_bytes,

@@ -102,6 +102,13 @@ def sparse_attn_workspace_bytes(B: int, S: int, H: int, D: int, K: int, num_spli
     return int(_load().sparse_attn_workspace_bytes(B, S, H, D, K, num_splits))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned uint8 device buffer of `nbytes` bytes, usable as sparse_attn's workspace."""
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + nbytes]
+
+
 def _workspace(device: torch.device, nbytes: int, workspace: torch.Tensor | None):
     if nbytes == 0:
         return None, 0
@@ -124,7 +131,8 @@ def sparse_attn(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor, topk
     """o = sparse_attn(q, kv, attn_sink, topk_idxs, scale).
 
     q [B,S,H,D] bf16, kv [B,T,D] bf16, attn_sink [H] fp32, topk_idxs [B,S,K] int32
-    (-1 = empty slot); returns o [B,S,H,D] bf16. num_splits = 0 lets the library choose.
+    (-1 = empty slot); returns o [B,S,H,D] bf16. num_splits = 0 lets the library choose;
+    `workspace` (uint8, 256-byte aligned, see new_workspace) overrides the cached one.
     """
     dev = q.device
     _check(q, "q", torch.bfloat16)

@@ -11,6 +11,7 @@ int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, 
                               int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
                               int nsplit, void* ws, void* stream);
 int sa_internal_head_blocks(int64_t H);
+size_t sa_internal_sparse_ws_bytes(int64_t ntok, int64_t H, int64_t D, int nsplit);
 int sa_internal_launch_bitmask(const int32_t* idx, const int32_t* q_lens, const int32_t* key_starts, uint32_t* mask,
                                int64_t B, int64_t Q, int64_t topk, int64_t key_len, int64_t padded_q, int64_t words,
                                void* stream);
@@ -47,10 +48,7 @@ int choose_splits(int64_t B, int64_t S, int64_t K, int requested) {
 
 size_t sparse_ws_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int nsplit) {
   if (nsplit <= 1) return 0;
-  const int64_t hp = (int64_t)sa_internal_head_blocks(H) * 16;
-  const int64_t pairs = B * S * nsplit;
-  // bf16 normalised partial outputs, then one fp32 log-sum-exp per (split, head)
-  return (size_t)(pairs * hp * D) * 2 + (size_t)(pairs * hp) * sizeof(float);
+  return sa_internal_sparse_ws_bytes(B * S, H, D, nsplit);
 }
 
 }  // namespace

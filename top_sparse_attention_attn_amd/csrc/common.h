@@ -104,9 +104,9 @@ __device__ __forceinline__ float sum4_x16_x32(float v) {
 }
 
 // Map a linear workgroup id so that consecutive logical ids land on the same XCD
-// (workgroups are dispatched round-robin over the 8 XCDs).
-__device__ __forceinline__ int xcd_local_id(int id, int n) {
-  return (n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id;
+// (workgroups are dispatched round-robin over the nx XCDs).
+__device__ __forceinline__ int xcd_local_id(int id, int n, int nx = 8) {
+  return (nx > 1 && n % nx == 0) ? (id % nx) * (n / nx) + id / nx : id;
 }
 
 }  // namespace sa

@@ -26,6 +26,8 @@
 //  * Online softmax in base 2 with a lazily moved reference maximum: the output is
 //    rescaled only when a head's maximum grows by more than 2^8 (rare after the first
 //    tile); weights stay <= 2^8, so nothing overflows.
+#include <stddef.h>
+
 #include "common.h"
 
 namespace sa {
@@ -64,6 +66,7 @@ struct Smem {
   float lsum[HB * 16];
   float alpha[2][HB * 16];
   float fin[HB * 16];
+  float lsef[HB * 16];  // log-sum-exp (log2 units) of this split's weights per head
   unsigned char vmb[kBufs][8];  // per value wave: validity of its 4 rows of the tile (one byte each)
   int flag[2][4];
 };
@@ -121,7 +124,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
                                           const float* __restrict__ sink, const int* __restrict__ idx,
                                           __bf16* __restrict__ out, __bf16* __restrict__ ws_o,
                                           float* __restrict__ ws_lse, int S, int H, int T, int K, int nsplit,
-                                          float scale_log2) {
+                                          int nxcc, float scale_log2) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
   constexpr int NB = SCORE ? 0 : G::kDBV;  // output column blocks of this wave
@@ -138,7 +141,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   const int db0 = SCORE ? 0 : sw * G::kDBV;
   const bool pv_active = !SCORE && db0 < G::kNDB;
 
-  const int pair = xcd_local_id(blockIdx.x, gridDim.x);
+  const int pair = xcd_local_id(blockIdx.x, gridDim.x, nxcc);
   const int tok = pair / nsplit, split = pair % nsplit;
   const int b = tok / S;
   const int ntiles_all = (K + kTile - 1) / kTile;
@@ -367,23 +370,17 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     }
   }
 
-  // ---- per-head totals (score waves): sum the partial row sums over the 4 lane groups
-  if constexpr (SCORE) {
-#pragma unroll
-    for (int qi = 0; qi < QB; qi++) l_fin[qi] = sm.lsum[(sw + 4 * qi) * 16 + l16];
-  }
-
   // Per-head output factor f (score waves own the heads): with no split the sink is folded
-  // in, o = O 2^(m-M) / (l 2^(m-M) + 2^(sink-M)); with splits each split stores its own
-  // normalised output O / l (bf16) and lse = m + log2(l), merged later with the sink.
+  // in, o = O 2^(m-M) / (l 2^(m-M) + 2^(sink-M)); with splits each split keeps its own
+  // normalised output O / l (bf16) and lse = m + log2(l), merged afterwards with the sink.
   if constexpr (SCORE) {
 #pragma unroll
     for (int qi = 0; qi < QB; qi++) {
       if (qi >= nq) break;
       const int h = (sw + 4 * qi) * 16 + l16;
       const float m = sm.mref[h];
-      const float l = l_fin[qi];
-      float f = 0.f;
+      const float l = sm.lsum[h];
+      float f = 0.f, lse = kNegInf;
       if (nsplit == 1) {
         if (h < H) {
           const float sk = sink[h];
@@ -401,33 +398,27 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
             }
           }
         }
-      } else {
-        f = (m > kNegInf && l > 0.f) ? 1.f / l : 0.f;
-        if (g == 0) ws_lse[(size_t)pair * HP + h] = (m > kNegInf && l > 0.f) ? m + __builtin_log2f(l) : kNegInf;
+      } else if (m > kNegInf && l > 0.f) {
+        f = 1.f / l;
+        lse = m + __builtin_log2f(l);
       }
-      if (g == 0) sm.fin[h] = f;
+      if (g == 0) {
+        sm.fin[h] = f;
+        sm.lsef[h] = lse;
+      }
     }
   }
   wait_lgkm0();
-  wg_barrier();
+  wg_barrier();  // every wave is past its last tile: the row ring is free for staging
+
+  // ---- stage this split's output in the row ring as bf16 with the factor applied:
+  //   no split: rows [h][D + 16] of the final output;
+  //   splits:   the MFMA layout [head block][d block][lane][4 heads] of the normalised partial.
+  __bf16* const stg = (__bf16*)&sm.kv[0][0];
+  constexpr int kOS = D + 16;  // staged row stride (bf16): 8 banks of skew per row
+  static_assert(HP * kOS * 2 <= (int)sizeof(sm.kv) && HP * D * 2 <= (int)sizeof(sm.kv), "staging exceeds the ring");
   if constexpr (NB > 0) {
-    if (!pv_active) return;
-    if (nsplit == 1) {
-#pragma unroll
-      for (int hb = 0; hb < HB; hb++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int h = hb * 16 + 4 * g + i;
-          if (h >= H) continue;
-          const float f = sm.fin[h];
-          __bf16* orow = out + ((size_t)tok * H + h) * D + db0 * 16 + l16;
-#pragma unroll
-          for (int db = 0; db < NB; db++) orow[db * 16] = (__bf16)(oacc[hb][db][i] * f);
-        }
-    } else {
-      // Split partial: block (hb, db) of normalised accumulators as bf16, 8 bytes per lane,
-      // at ws_o[pair][hb][db][lane][0..3].
-      bf16x4* wo = (bf16x4*)(ws_o + (size_t)pair * HP * D) + lane;
+    if (pv_active) {
 #pragma unroll
       for (int hb = 0; hb < HB; hb++) {
         float f[4];
@@ -435,26 +426,48 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         for (int i = 0; i < 4; i++) f[i] = sm.fin[hb * 16 + 4 * g + i];
 #pragma unroll
         for (int db = 0; db < NB; db++) {
-          bf16x4 v;
+          if (nsplit == 1) {
 #pragma unroll
-          for (int i = 0; i < 4; i++) v[i] = (__bf16)(oacc[hb][db][i] * f[i]);
-          wo[(hb * G::kNDB + db0 + db) * 64] = v;
+            for (int i = 0; i < 4; i++)
+              stg[(hb * 16 + 4 * g + i) * kOS + (db0 + db) * 16 + l16] = (__bf16)(oacc[hb][db][i] * f[i]);
+          } else {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[i] = (__bf16)(oacc[hb][db][i] * f[i]);
+            *(bf16x4*)(&stg[((hb * G::kNDB + db0 + db) * 64 + lane) * 4]) = v;
+          }
         }
       }
     }
   }
+  wait_lgkm0();
+  wg_barrier();
+  const int tid = threadIdx.x;
+  if (nsplit == 1) {  // final rows, 16-byte stores
+    constexpr int kRC = D / 8;
+    for (int c = tid; c < HP * kRC; c += kThreads) {
+      const int r = c / kRC, k = c % kRC;
+      if (r < H) *(uint4*)(out + ((size_t)tok * H + r) * D + 8 * k) = *(const uint4*)(&stg[r * kOS + 8 * k]);
+    }
+    return;
+  }
+  // split partial: the normalised block in MFMA layout and the log-sum-exps, merged with the
+  // other splits of the token (and the sink) by sparse_attn_combine_kernel
+  __bf16* const wpart = ws_o + (size_t)pair * HP * D;
+  for (int c = tid; c < HP * D / 8; c += kThreads) ((uint4*)wpart)[c] = ((const uint4*)stg)[c];
+  if (tid < HP) ws_lse[(size_t)pair * HP + tid] = sm.lsef[tid];
 }
 
 template <int D, int HB>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv, const float* __restrict__ sink,
     const int* __restrict__ idx, __bf16* __restrict__ out, __bf16* __restrict__ ws_o, float* __restrict__ ws_lse,
-    int S, int H, int T, int K, int nsplit, float scale_log2) {
+    int S, int H, int T, int K, int nsplit, int nxcc, float scale_log2) {
   __shared__ __attribute__((aligned(16))) Smem<D, HB> sm;
   if (threadIdx.x < 256)  // waves 0-3
-    run_split<D, HB, true>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, scale_log2);
+    run_split<D, HB, true>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, scale_log2);
   else
-    run_split<D, HB, false>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, scale_log2);
+    run_split<D, HB, false>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, scale_log2);
 }
 
 // Merge the split partials of one (token, 16-head block) and add the sink once:
@@ -467,7 +480,8 @@ template <int D, int HB>
 __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* __restrict__ ws_o,
                                                                    const float* __restrict__ ws_lse,
                                                                    const float* __restrict__ sink,
-                                                                   __bf16* __restrict__ out, int H, int nsplit) {
+                                                                   __bf16* __restrict__ out, int H, int nsplit,
+                                                                   int nxcc) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
   constexpr int kChunks = G::kNDB * 64 * 8 / 16;       // 16-byte chunks of one partial block
@@ -475,7 +489,7 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* 
   constexpr int kOutStride = D + 8;                    // bf16 per staged output row
   __shared__ float wgt[kMaxSplits * 16];
   __shared__ __attribute__((aligned(16))) __bf16 stage[16 * kOutStride];
-  const int blk = xcd_local_id(blockIdx.x, gridDim.x);
+  const int blk = xcd_local_id(blockIdx.x, gridDim.x, nxcc);
   const int tok = blk / HB, hb = blk % HB;
   const int t = threadIdx.x;
 
@@ -568,21 +582,51 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* 
   }
 }
 
+// Workspace of a split call: bf16 partials [pair][HP*D], then fp32 log-sum-exps [pair][HP]
+// (256-byte aligned parts). Pure scratch: contents on entry do not matter.
+struct WsLayout {
+  size_t lse, total;
+};
+static inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+static WsLayout ws_layout(int64_t ntok, int64_t HB, int64_t D, int nsplit) {
+  WsLayout w{};
+  if (nsplit <= 1) return w;
+  const size_t pairs = (size_t)ntok * nsplit, hp = (size_t)HB * 16;
+  w.lse = round256(pairs * hp * D * 2);
+  w.total = w.lse + round256(pairs * hp * 4);
+  return w;
+}
+
+// XCDs of the current device (workgroups are dispatched round-robin over them).
+static int device_xccs() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  if (cache[dev] == 0) {
+    int v = 1;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || v < 1) v = 1;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
 template <int D, int HB>
 static hipError_t launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
                                 int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int nsplit,
                                 void* ws, hipStream_t stream) {
   const int64_t ntok = B * S;
-  constexpr int HP = HB * 16;
-  __bf16* ws_o = (__bf16*)ws;
-  float* ws_lse = ws_o == nullptr ? nullptr : (float*)(ws_o + (size_t)ntok * nsplit * HP * D);
-  hipLaunchKernelGGL((sparse_attn_kernel<D, HB>), dim3((unsigned)(ntok * nsplit)), dim3(kThreads), 0, stream,
-                     (const __bf16*)q, (const __bf16*)kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H,
-                     (int)T, (int)K, nsplit, scale * kLog2e);
+  const int64_t n = ntok * nsplit;
+  const WsLayout L = ws_layout(ntok, HB, D, nsplit);
+  __bf16* ws_o = nsplit > 1 ? (__bf16*)ws : nullptr;
+  float* ws_lse = nsplit > 1 ? (float*)((char*)ws + L.lse) : nullptr;
+  const int nxcc = device_xccs();
+  hipLaunchKernelGGL((sparse_attn_kernel<D, HB>), dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q,
+                     (const __bf16*)kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H, (int)T, (int)K, nsplit,
+                     nxcc, scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)(ntok * HB)), dim3(256), 0, stream, ws_o, ws_lse,
-                     sink, (__bf16*)out, (int)H, nsplit);
+                     sink, (__bf16*)out, (int)H, nsplit, nxcc);
   return hipGetLastError();
 }
 
@@ -608,4 +652,9 @@ extern "C" int sa_internal_launch_sparse(const void* q, const void* kv, const fl
   }
 #undef SA_CASE
   return e == hipSuccess ? 0 : 1;
+}
+
+// Workspace bytes of a split call (see WsLayout).
+extern "C" size_t sa_internal_sparse_ws_bytes(int64_t ntok, int64_t H, int64_t D, int nsplit) {
+  return sa::ws_layout(ntok, sa_internal_head_blocks(H), D, nsplit).total;
 }
