@@ -58,15 +58,36 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
 
 
-def sparse_work(inp) -> tuple[float, float]:
-    """Algorithmic bytes and flops of one sparse_attn call: gathered valid rows, q, o, indices."""
+def sparse_work(inp, nsplit: int) -> tuple[float, float, float]:
+    """Algorithmic bytes and flops of one sparse_attn call (gathered valid rows, q, o, indices),
+    and the algorithmic bytes of its main kernel alone (the same without o when the call has
+    split partials, whose merge kernel writes o)."""
     q, idx = inp["q"], inp["topk_idxs"]
     B, S, H, D = q.shape
     T = inp["kv"].shape[1]
     n_valid = int(((idx >= 0) & (idx < T)).sum().item())
     nbytes = n_valid * D * 2 + 2 * B * S * H * D * 2 + idx.numel() * 4
     flops = 4.0 * H * D * n_valid
-    return float(nbytes), flops
+    main_bytes = nbytes - (B * S * H * D * 2 if nsplit > 1 else 0)
+    return float(nbytes), flops, float(main_bytes)
+
+
+def measured_traffic(config: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain copy of known size),
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"counters_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    from top_sparse_attention_attn_amd.profile_summary import kernel_sources_sha256
+
+    if c.get("source_sha256") != kernel_sources_sha256():
+        return None
+    ff = c["copy_bytes"] / (c["copy_fetch_kib"] * 1024.0)
+    fw = c["copy_bytes"] / (c["copy_write_kib"] * 1024.0)
+    return c["fetch_kib_per_launch"] * 1024.0 * ff + c["write_kib_per_launch"] * 1024.0 * fw
 
 
 def masked_work(inp, mask_bytes: int) -> tuple[float, float]:
@@ -123,11 +144,19 @@ def main():
         ws_bytes = sa.sparse_attn_workspace_bytes(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)
         ws = sa.new_workspace(ws_bytes, dev)
 
+        nsplit = sa.sparse_attn_num_splits(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)
+
         def step(i):
             x = sets[i % nsets]
             sa.sparse_attn(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
 
-        work = [sparse_work(x) for x in sets]
+        def kernel_step(i):  # the main kernel alone (the first of the call's two phases)
+            x = sets[i % nsets]
+            sa.sparse_attn_split(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
+
+        hb = 1 if cfg.H <= 16 else (2 if cfg.H <= 32 else (4 if cfg.H <= 64 else 8))
+        kernel_name = f"sparse_attn_kernel<{cfg.D},{hb}>"
+        work = [sparse_work(x, nsplit) for x in sets]
         units_per_step = cfg.B * cfg.S
         unit = "query-tokens/s"
         bound = "hbm" if args.config in ("decode", "ragged", "tiny") else "mfma"
@@ -157,7 +186,9 @@ def main():
                 x = sets[i % nsets]
                 sa.masked_attn(x["q"], x["k"], x["v"], masks[i % nsets], x["scale"], out=out)
 
+            kernel_step, kernel_name = step, "masked_attn_kernel<192,128,128>"
             work = [masked_work(x, masks[0].numel() * 4) for x in sets]
+            work = [(w[0], w[1], w[0]) for w in work]
             units_per_step = cfg.B * cfg.Q
             unit = "query-tokens/s"
             bound = "mfma"
@@ -178,7 +209,9 @@ def main():
                 x = sets[i % nsets]
                 sa.topk_bitmask_build(x["topk_idxs"], cfg.KV, out=outm)
 
+            kernel_step, kernel_name = step, "topk_bitmask_kernel"
             work = [(float(x["topk_idxs"].numel() * 4 + masks[0].numel() * 4), 0.0) for x in sets]
+            work = [(w[0], w[1], w[0]) for w in work]
             units_per_step = cfg.B * cfg.Q
             unit = "query-rows/s"
             bound = "hbm"
@@ -204,18 +237,34 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
+    # The dominant kernel alone, timed the same way on the same stream.
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        kernel_step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kms = e0.elapsed_time(e1) / args.steps
+
     nbytes = sum(w[0] for w in work) / len(work)
     flops = sum(w[1] for w in work) / len(work)
+    kbytes = sum(w[2] for w in work) / len(work)
     if bound == "hbm":
-        achieved = nbytes / (ms * 1e-3) / 1e9
+        achieved = kbytes / (kms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+                "frac": achieved / HBM_PEAK_GBS}
+        call_frac = nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     else:
-        achieved = flops / (ms * 1e-3) / 1e12
+        achieved = flops / (kms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
-    roof["alg_bytes_per_call"] = nbytes
-    roof["alg_flops_per_call"] = flops
+                "frac": achieved / BF16_PEAK_TFLOPS}
+        call_frac = flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+    roof["traffic"] = measured_traffic(args.config)
+    roof["kernel"] = kernel_name
+    roof["kernel_ms"] = kms
+    roof["alg_bytes_per_launch"] = kbytes
+    roof["alg_flops_per_launch"] = flops
+    roof["call_frac"] = call_frac  # the whole call (every kernel of one step) against the same peak
 
     cpu = None
     if not args.no_cpu_baseline:

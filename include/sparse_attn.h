@@ -96,6 +96,26 @@ int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const
                     int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The two phases of sparse_attn_fwd, for callers that schedule them apart (to
+ * overlap the merge with other work) or time them: sparse_attn_split_fwd runs
+ * the attention over each token's split slot ranges and leaves normalised
+ * partial outputs and their log-sum-exps in the workspace; sparse_attn_merge_fwd
+ * merges them into `out`, adding the sink once (the identity: the split at
+ * log-sum-exp e_p weighs 2^(e_p - M) / (sum_p 2^(e_p - M) + 2^(sink log2 e - M))).
+ * When the split count resolves to 1, sparse_attn_split_fwd writes `out` in full
+ * and sparse_attn_merge_fwd does nothing. Both take exactly sparse_attn_fwd's
+ * arguments and checks; call them in this order on one stream with the same
+ * arguments and workspace. Combined merge identity: DeepSeek V4 source notes,
+ * ch. 5, section 5.5 (FlashMLA's split combine with the sink).
+ */
+int sparse_attn_split_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                          int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int sparse_attn_merge_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                          int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Bit-packed top-k mask.                                                    */
 /* Shape rule and row layout: prhub summary of vLLM PR #52217, key source    */

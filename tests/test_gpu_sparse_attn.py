@@ -244,3 +244,17 @@ def test_split_merge_special_cases():
     assert torch.equal(out[1, 0, 2:], inp["kv"][1, 17].expand(126, 512))
     assert torch.count_nonzero(out[:, :, 0]).item() == 0
     assert torch.isnan(out[:, :, 1]).all()
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_split_then_merge_equals_one_call(splits):
+    """The two phases called apart give exactly the one-call result."""
+    inp = _custom(16, 1, 128, 512, 600, 512, seed=51)
+    ws = sa.new_workspace(sa.sparse_attn_workspace_bytes(16, 1, 128, 512, 512, splits), DEV)
+    a = _run(inp, num_splits=splits, workspace=ws)
+    b = torch.full_like(a, 7.0)
+    args = (inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    sa.sparse_attn_split(*args, out=b, num_splits=splits, workspace=ws)
+    sa.sparse_attn_merge(*args, out=b, num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

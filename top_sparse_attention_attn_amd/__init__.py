@@ -12,6 +12,8 @@ from .api import (  # noqa: F401
     masked_attn,
     new_workspace,
     sparse_attn,
+    sparse_attn_merge,
+    sparse_attn_split,
     sparse_attn_num_splits,
     sparse_attn_workspace_bytes,
     topk_bitmask_build,

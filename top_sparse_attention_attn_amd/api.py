@@ -22,7 +22,8 @@ SA_STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_ALIGN",
              5: "SA_ERR_WORKSPACE", 6: "SA_ERR_HIP"}
 
 EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_fwd",
-            "topk_bitmask_shape", "topk_bitmask_build", "masked_attn_fwd"]
+            "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "topk_bitmask_shape", "topk_bitmask_build",
+            "masked_attn_fwd"]
 
 
 class SparseAttnError(RuntimeError):
@@ -51,8 +52,9 @@ def _load():
         lib.sparse_attn_workspace_bytes.restype = ctypes.c_size_t
         lib.sparse_attn_num_splits.argtypes = [I64, I64, I64, I64, I64]
         lib.sparse_attn_num_splits.restype = I
-        lib.sparse_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
-        lib.sparse_attn_fwd.restype = I
+        for name in ("sparse_attn_fwd", "sparse_attn_split_fwd", "sparse_attn_merge_fwd"):
+            getattr(lib, name).argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
+            getattr(lib, name).restype = I
         lib.topk_bitmask_shape.argtypes = [I64, I64, I64, I, P]
         lib.topk_bitmask_shape.restype = I
         lib.topk_bitmask_build.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P]
@@ -134,6 +136,21 @@ def sparse_attn(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor, topk
     (-1 = empty slot); returns o [B,S,H,D] bf16. num_splits = 0 lets the library choose;
     `workspace` (uint8, 256-byte aligned, see new_workspace) overrides the cached one.
     """
+    return _sparse_call("sparse_attn_fwd", q, kv, attn_sink, topk_idxs, scale, out, num_splits, workspace)
+
+
+def sparse_attn_split(q, kv, attn_sink, topk_idxs, scale, out=None, num_splits: int = 0, workspace=None):
+    """First phase of sparse_attn (sparse_attn_split_fwd): split partials into `workspace`,
+    or the full output when the call has one split. Pass the same workspace to sparse_attn_merge."""
+    return _sparse_call("sparse_attn_split_fwd", q, kv, attn_sink, topk_idxs, scale, out, num_splits, workspace)
+
+
+def sparse_attn_merge(q, kv, attn_sink, topk_idxs, scale, out, num_splits: int = 0, workspace=None):
+    """Second phase of sparse_attn (sparse_attn_merge_fwd): merge the partials into `out`."""
+    return _sparse_call("sparse_attn_merge_fwd", q, kv, attn_sink, topk_idxs, scale, out, num_splits, workspace)
+
+
+def _sparse_call(entry, q, kv, attn_sink, topk_idxs, scale, out, num_splits, workspace):
     dev = q.device
     _check(q, "q", torch.bfloat16)
     _check(kv, "kv", torch.bfloat16, dev)
@@ -154,7 +171,7 @@ def sparse_attn(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor, topk
             raise ValueError("out must have q's shape")
     need = sparse_attn_workspace_bytes(B, S, H, D, K, num_splits)
     ws, ws_bytes = _workspace(dev, need, workspace)
-    _call("sparse_attn_fwd", _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, S, H, D, T, K,
+    _call(entry, _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, S, H, D, T, K,
           float(scale), int(num_splits), _ptr(ws), ws_bytes, _stream_ptr(dev))
     return out
 

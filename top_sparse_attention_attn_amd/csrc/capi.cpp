@@ -9,7 +9,7 @@
 extern "C" {
 int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
                               int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
-                              int nsplit, void* ws, void* stream);
+                              int nsplit, void* ws, int phases, void* stream);
 int sa_internal_head_blocks(int64_t H);
 size_t sa_internal_sparse_ws_bytes(int64_t ntok, int64_t H, int64_t D, int nsplit);
 int sa_internal_launch_bitmask(const int32_t* idx, const int32_t* q_lens, const int32_t* key_starts, uint32_t* mask,
@@ -51,6 +51,28 @@ size_t sparse_ws_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int nsplit) {
   return sa_internal_sparse_ws_bytes(B * S, H, D, nsplit);
 }
 
+static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                           int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
+                           int num_splits, void* workspace, size_t workspace_bytes, void* stream, int phases) {
+  if (!sparse_sizes_ok(B, S, H, D, K) || T < 0 || num_splits < 0 || num_splits > 64) return SA_ERR_SHAPE;
+  if (B * S == 0 || H == 0) return SA_OK;
+  if (D != 64 && D != 512) return SA_ERR_UNSUPPORTED;
+  if (H > 128) return SA_ERR_UNSUPPORTED;
+  if (B * S > (int64_t)1 << 30 || T > (int64_t)1 << 31 || K > (int64_t)1 << 30) return SA_ERR_SHAPE;
+  if (!q || !attn_sink || !out || (K > 0 && !topk_idxs) || (T > 0 && K > 0 && !kv)) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (kv && !aligned16(kv))) return SA_ERR_ALIGN;
+  if (((uintptr_t)attn_sink & 3u) || (topk_idxs && ((uintptr_t)topk_idxs & 3u))) return SA_ERR_ALIGN;
+  const int nsplit = choose_splits(B, S, K, num_splits);
+  const size_t need = sparse_ws_bytes(B, S, H, D, nsplit);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return SA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255u) return SA_ERR_ALIGN;
+  }
+  const int rc = sa_internal_launch_sparse(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, nsplit,
+                                           need > 0 ? workspace : nullptr, phases, stream);
+  return rc == 0 ? SA_OK : SA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,23 +104,22 @@ size_t sparse_attn_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, i
 int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
                     int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (!sparse_sizes_ok(B, S, H, D, K) || T < 0 || num_splits < 0 || num_splits > 64) return SA_ERR_SHAPE;
-  if (B * S == 0 || H == 0) return SA_OK;
-  if (D != 64 && D != 512) return SA_ERR_UNSUPPORTED;
-  if (H > 128) return SA_ERR_UNSUPPORTED;
-  if (B * S > (int64_t)1 << 30 || T > (int64_t)1 << 31 || K > (int64_t)1 << 30) return SA_ERR_SHAPE;
-  if (!q || !attn_sink || !out || (K > 0 && !topk_idxs) || (T > 0 && K > 0 && !kv)) return SA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || (kv && !aligned16(kv))) return SA_ERR_ALIGN;
-  if (((uintptr_t)attn_sink & 3u) || (topk_idxs && ((uintptr_t)topk_idxs & 3u))) return SA_ERR_ALIGN;
-  const int nsplit = choose_splits(B, S, K, num_splits);
-  const size_t need = sparse_ws_bytes(B, S, H, D, nsplit);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return SA_ERR_WORKSPACE;
-    if ((uintptr_t)workspace & 255u) return SA_ERR_ALIGN;
-  }
-  const int rc = sa_internal_launch_sparse(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, nsplit,
-                                           need > 0 ? workspace : nullptr, stream);
-  return rc == 0 ? SA_OK : SA_ERR_HIP;
+  return sparse_attn_run(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, num_splits, workspace,
+                         workspace_bytes, stream, 3);
+}
+
+int sparse_attn_split_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                          int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attn_run(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, num_splits, workspace,
+                         workspace_bytes, stream, 1);
+}
+
+int sparse_attn_merge_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                          int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attn_run(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, num_splits, workspace,
+                         workspace_bytes, stream, 2);
 }
 
 int topk_bitmask_shape(int64_t B, int64_t max_q_len, int64_t max_key_len, int reserve_key_start_word,

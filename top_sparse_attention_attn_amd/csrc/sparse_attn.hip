@@ -613,18 +613,21 @@ static int device_xccs() {
 template <int D, int HB>
 static hipError_t launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
                                 int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int nsplit,
-                                void* ws, hipStream_t stream) {
+                                void* ws, int phases, hipStream_t stream) {
   const int64_t ntok = B * S;
   const int64_t n = ntok * nsplit;
   const WsLayout L = ws_layout(ntok, HB, D, nsplit);
   __bf16* ws_o = nsplit > 1 ? (__bf16*)ws : nullptr;
   float* ws_lse = nsplit > 1 ? (float*)((char*)ws + L.lse) : nullptr;
   const int nxcc = device_xccs();
-  hipLaunchKernelGGL((sparse_attn_kernel<D, HB>), dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q,
-                     (const __bf16*)kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H, (int)T, (int)K, nsplit,
-                     nxcc, scale * kLog2e);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
+  if (phases & 1) {
+    hipLaunchKernelGGL((sparse_attn_kernel<D, HB>), dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q,
+                       (const __bf16*)kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H, (int)T, (int)K, nsplit,
+                       nxcc, scale * kLog2e);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nsplit == 1 || !(phases & 2)) return hipSuccess;
   hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)(ntok * HB)), dim3(256), 0, stream, ws_o, ws_lse,
                      sink, (__bf16*)out, (int)H, nsplit, nxcc);
   return hipGetLastError();
@@ -638,13 +641,15 @@ extern "C" int sa_internal_head_blocks(int64_t H) {
   return hb <= 2 ? hb : (hb <= 4 ? 4 : 8);
 }
 
+// phases: bit 0 = the main kernel, bit 1 = the merge of the split partials (if any)
 extern "C" int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx,
                                          void* out, int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K,
-                                         float scale, int nsplit, void* ws, void* stream) {
+                                         float scale, int nsplit, void* ws, int phases, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int hb = sa_internal_head_blocks(H);
   hipError_t e;
-#define SA_CASE(DD, HBB) e = sa::launch_sparse<DD, HBB>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, st)
+#define SA_CASE(DD, HBB) \
+  e = sa::launch_sparse<DD, HBB>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, phases, st)
   if (D == 512) {
     if (hb == 1) SA_CASE(512, 1); else if (hb == 2) SA_CASE(512, 2); else if (hb == 4) SA_CASE(512, 4); else SA_CASE(512, 8);
   } else {
