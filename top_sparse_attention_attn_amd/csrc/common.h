@@ -24,6 +24,41 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(VM >= 0 && VM < 64, "vmcnt out of range");
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (V#) for raw, untyped loads of [base, base + bytes); base wave-uniform.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu;  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000u;  // 32-bit data format, no swizzle
+  return r;
+}
+
+// Byte address in the workgroup's LDS of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)p);
+}
+
+// Raw buffer loads into LDS (16 or 4 bytes per lane): lane L's bytes at offset `off` of the
+// resource land at LDS address m0addr + 16 L (or 4 L); an offset at or past the resource's size
+// reads nothing. Written as inline assembly so that the compiler adds no wait for them before
+// later LDS reads (it cannot tell which LDS bytes they write): the caller waits (s_waitcnt
+// vmcnt, then a barrier) before the destination is read.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_lds16(u32x4 rs, uint32_t off, uint32_t m0addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0addr), "v"(off), "s"(rs) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(u32x4 rs, uint32_t off, uint32_t m0addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m0addr), "v"(off), "s"(rs) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // s_waitcnt lgkmcnt(0) only (vector memory left in flight).
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8)); }
 
