@@ -15,6 +15,8 @@ Sources, per function:
   topk_mask_build      same page (_build_topk_mask + its test) and prhub summary of
                        vLLM PR #48770, key source (dense_mask_mod, offset_dense_mask_mod)
   masked_attn          prhub summary of vLLM PR #48770 (masked-MHA path) and PR #52217
+  masked_attn_offset   prhub summary of vLLM PR #48770, key source (offset_dense_mask_mod:
+                       chunked context, key index + key_start from the reserved word)
 """
 from __future__ import annotations
 
@@ -60,6 +62,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_topk_mask_build.restype = ctypes.c_int
     lib.oracle_masked_attn.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, ctypes.c_double, P, I]
     lib.oracle_masked_attn.restype = ctypes.c_int
+    lib.oracle_masked_attn_offset.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, ctypes.c_double, P, I]
+    lib.oracle_masked_attn_offset.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -78,7 +82,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
 
 
 class Oracle:
-    """The oracle's four operations, bound to one compiled copy of the C source."""
+    """The oracle's operations, bound to one compiled copy of the C source."""
 
     def __init__(self, lib: ctypes.CDLL | None = None):
         self.lib = lib if lib is not None else load()
@@ -150,6 +154,17 @@ class Oracle:
         q_bits [B,Q,H,Dqk], k_bits [B,KV,H,Dqk], v_bits [B,KV,H,Dv] uint16; mask
         [B,padded_q,W] uint32 or None (every key visible). Returns float64 [len(rows), H, Dv].
         """
+        return self._masked(self.lib.oracle_masked_attn, q_bits, k_bits, v_bits, mask, scale, rows)
+
+    def masked_attn_offset(self, q_bits, k_bits, v_bits, mask, scale, rows=None) -> np.ndarray:
+        """The chunked-context form: chunk key j is mask key key_start[b] + j, with key_start[b]
+        the reserved word mask[b, 0, W-1]; keys at or past that word are never visible.
+        Arguments and result as masked_attn (mask required)."""
+        if mask is None:
+            raise ValueError("masked_attn_offset oracle: the mask is required")
+        return self._masked(self.lib.oracle_masked_attn_offset, q_bits, k_bits, v_bits, mask, scale, rows)
+
+    def _masked(self, fn, q_bits, k_bits, v_bits, mask, scale, rows):
         q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
         k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
         v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
@@ -168,7 +183,7 @@ class Oracle:
             rows = np.arange(B * Q, dtype=np.int64)
         rows = np.ascontiguousarray(rows, dtype=np.int64)
         out = np.empty((len(rows), H, Dv), dtype=np.float64)
-        rc = self.lib.oracle_masked_attn(
+        rc = fn(
             self._ptr(q_bits), self._ptr(k_bits), self._ptr(v_bits), self._ptr(mask), self._ptr(out),
             B, Q, KV, H, Dqk, Dv, padded_q, W, float(scale), self._ptr(rows), len(rows))
         if rc != 0:

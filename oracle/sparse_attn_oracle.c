@@ -25,7 +25,7 @@
  *  [PR48770] prhub summary of vLLM PR #48770 "masked MHA for sparse MLA
  *            prefill": key-source section (dense_mask_mod: word = kv >> 5,
  *            bit = kv & 31, LSB first; offset_dense_mask_mod reads key_start
- *            from the last word of query row 0).
+ *            from the last word of query row 0 and adds it to the key index).
  *
  * Parity pins for every function here live in tests/test_oracle_pins.py.
  */
@@ -233,13 +233,23 @@ int oracle_topk_mask_build(const int32_t* idx, const int32_t* q_lens, const int3
  *   J = { j < KV : mask is NULL or bit (j & 31) of mask[b][qi][j >> 5] is set }
  *   x_j = scale * q.k_j;  o = sum_{j in J} softmax(x)_j v_j   (max subtracted first)
  *   J empty -> o = 0.  No sink, one mask shared by every head.
+ *
+ * Chunked-context form ([PR48770] offset_dense_mask_mod), offset != 0: k and v are
+ * one chunk of a longer context and chunk key j is key p = key_start + j of the mask
+ * row, with key_start[b] = mask[b][0][W-1] (the reserved word, read as an unsigned
+ * 32-bit value):
+ *   J = { j < KV : p < 32 (W - 1) and bit (p & 31) of mask[b][qi][p >> 5] is set }.
+ * Positions at or past the reserved word are never visible (that word holds the
+ * start, not bits).
  */
-int oracle_masked_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* mask, double* out,
-                       int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q, int64_t W,
-                       double scale, const int64_t* rows, int64_t nrows) {
+static int masked_attn_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* mask,
+                            double* out, int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv,
+                            int64_t padded_q, int64_t W, double scale, const int64_t* rows, int64_t nrows,
+                            int offset) {
   if (!q || !k || !v || !out || !rows) return -1;
   if (B < 0 || Q < 0 || KV < 0 || H < 0 || Dqk < 0 || Dv < 0 || nrows < 0) return -1;
-  if (mask && (padded_q < Q || W * 32 < KV)) return -1;
+  if (mask && (padded_q < Q || (!offset && W * 32 < KV))) return -1;
+  if (offset && (!mask || W < 1)) return -1;
   for (int64_t i = 0; i < nrows; i++)
     if (rows[i] < 0 || rows[i] >= B * Q) return -1;
 
@@ -250,12 +260,33 @@ int oracle_masked_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     const uint32_t* mrow = mask ? mask + (b * padded_q + qi) * W : NULL;
     double* x = (double*)malloc(sizeof(double) * (size_t)(KV > 0 ? KV : 1));
     char* vis = (char*)malloc((size_t)(KV > 0 ? KV : 1));
-    for (int64_t j = 0; j < KV; j++) {
-#if ORACLE_MUTANT == 9
-      vis[j] = 1; /* mutant: mask ignored */
+    if (offset) {
+#if ORACLE_MUTANT == 14
+      const uint64_t key_start = mrow[W - 1]; /* mutant: start read from the query's own row */
 #else
-      vis[j] = mrow ? (char)((mrow[j >> 5] >> (j & 31)) & 1u) : 1;
+      const uint64_t key_start = mask[(b * padded_q + 0) * W + (W - 1)];
 #endif
+      const uint64_t limit = 32u * (uint64_t)(W - 1);
+      for (int64_t j = 0; j < KV; j++) {
+#if ORACLE_MUTANT == 13
+        const uint64_t p = (uint64_t)j; /* mutant: start ignored */
+#else
+        const uint64_t p = key_start + (uint64_t)j;
+#endif
+#if ORACLE_MUTANT == 15
+        vis[j] = p < 32u * (uint64_t)W ? (char)((mrow[p >> 5] >> (p & 31)) & 1u) : 0; /* mutant: reserved word read as bits */
+#else
+        vis[j] = p < limit ? (char)((mrow[p >> 5] >> (p & 31)) & 1u) : 0;
+#endif
+      }
+    } else {
+      for (int64_t j = 0; j < KV; j++) {
+#if ORACLE_MUTANT == 9
+        vis[j] = 1; /* mutant: mask ignored */
+#else
+        vis[j] = mrow ? (char)((mrow[j >> 5] >> (j & 31)) & 1u) : 1;
+#endif
+      }
     }
     for (int64_t h = 0; h < H; h++) {
       const uint16_t* qv = q + ((b * Q + qi) * H + h) * Dqk;
@@ -293,6 +324,18 @@ int oracle_masked_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     free(vis);
   }
   return 0;
+}
+
+int oracle_masked_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* mask, double* out,
+                       int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q, int64_t W,
+                       double scale, const int64_t* rows, int64_t nrows) {
+  return masked_attn_impl(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, W, scale, rows, nrows, 0);
+}
+
+int oracle_masked_attn_offset(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* mask,
+                              double* out, int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv,
+                              int64_t padded_q, int64_t W, double scale, const int64_t* rows, int64_t nrows) {
+  return masked_attn_impl(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, W, scale, rows, nrows, 1);
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */

@@ -410,10 +410,76 @@ def check_two_forms_agree(o):
     assert np.abs(a - b).max() <= 1e-13
 
 
+def _offset_case(seed, key_len, key_start, KV, B=2, Q=4, H=2, Dqk=24, Dv=16, W=None, density=0.4):
+    """Random boolean visibility over a global context of key_len keys, packed by hand
+    (not by the oracle's builder) with key_start in the reserved word, and a chunk of KV
+    keys' k and v."""
+    g = np.random.default_rng(seed)
+    W = W if W is not None else 4 * -(-(-(-key_len // 32) + 1) // 4)
+    bm = g.random((B, Q, key_len)) < density
+    mask = _pack(bm, W)
+    mask[:, 0, W - 1] = np.uint32(key_start)
+    q, k, v = _masked_tiny(seed, B=B, Q=Q, KV=KV, H=H, Dqk=Dqk, Dv=Dv)
+    return q, k, v, bm, mask, W
+
+
+def _sdpa_masked(q, k, v, bm, scale):
+    attn = torch.from_numpy(bm).unsqueeze(1)
+    ref = F.scaled_dot_product_attention(_f64(q).permute(0, 2, 1, 3), _f64(k).permute(0, 2, 1, 3),
+                                         _f64(v).permute(0, 2, 1, 3), attn_mask=attn, scale=scale)
+    return ref.permute(0, 2, 1, 3).numpy()
+
+
+def check_offset_chunk_is_sdpa(o):
+    """Chunked-context form: with key_start = 37 (not a multiple of 32) chunk key j sees global
+    key 37 + j; the result equals SDPA over the chunk with the global mask's columns 37..37+KV-1,
+    for every query row (row 0 holds the start; the other rows' last word is zero)."""
+    key_len, ks, KV = 200, 37, 100
+    q, k, v, bm, mask, W = _offset_case(21, key_len, ks, KV)
+    scale = 24 ** -0.5
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    got = o.masked_attn_offset(_bits(q), _bits(k), _bits(v), mask, scale).reshape(B, Q, H, -1)
+    sub = bm[:, :, ks:ks + KV]
+    ref = _sdpa_masked(q, k, v, sub, scale)
+    live = sub.any(axis=2)
+    assert live.all()
+    assert np.abs(got[live] - ref[live]).max() <= 1e-12
+
+
+def check_offset_zero_start_is_plain(o):
+    """key_start = 0 reduces the chunked form to the plain masked form (same mask bits)."""
+    q, k, v, bm, mask, W = _offset_case(22, 96, 0, 96)
+    scale = 24 ** -0.5
+    a = o.masked_attn_offset(_bits(q), _bits(k), _bits(v), mask, scale)
+    b = o.masked_attn(_bits(q), _bits(k), _bits(v), mask, scale)
+    assert np.array_equal(a, b)
+
+
+def check_offset_stops_at_reserved_word(o):
+    """Chunk keys whose global position falls at or past the reserved word are not visible:
+    with W = 8 (bit words 0..6 = keys 0..223), key_start 200 and a chunk of 40 keys, only chunk
+    keys 0..23 can be seen, although the reserved word's own bits (the start, 200) are set; a
+    start past every bit word leaves every row empty (o = 0)."""
+    key_len, ks, KV = 224, 200, 40
+    q, k, v, bm, mask, W = _offset_case(23, key_len, ks, KV, W=8, density=1.0)
+    assert W == 8 and mask[0, 0, 7] == 200
+    scale = 24 ** -0.5
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    got = o.masked_attn_offset(_bits(q), _bits(k), _bits(v), mask, scale).reshape(B, Q, H, -1)
+    sub = np.zeros((B, Q, KV), dtype=bool)
+    sub[:, :, :224 - ks] = True
+    ref = _sdpa_masked(q, k, v, sub, scale)
+    assert np.abs(got - ref).max() <= 1e-12
+    mask[:, 0, 7] = np.uint32(5000)
+    empty = o.masked_attn_offset(_bits(q), _bits(k), _bits(v), mask, scale)
+    assert np.all(empty == 0.0)
+
+
 SPARSE_PINS = [check_loop_semantics, check_all_invalid_zero, check_order_invariance, check_dense_equivalence,
                check_sink_extra_key, check_exact_mean, check_sink_halves, check_single_row, check_inf_nan_sink,
                check_huge_sink, check_duplicates_count, check_scale_closed_form, check_out_of_range_is_empty]
 MASK_PINS = [check_mask_worked_example, check_mask_brute_force, check_mask_single_equals_batched,
              check_mask_reserved_word]
-MASKED_PINS = [check_masked_dense, check_masked_random, check_two_forms_agree]
+MASKED_PINS = [check_masked_dense, check_masked_random, check_two_forms_agree, check_offset_chunk_is_sdpa,
+               check_offset_zero_start_is_plain, check_offset_stops_at_reserved_word]
 ALL_PINS = SPARSE_PINS + MASK_PINS + MASKED_PINS

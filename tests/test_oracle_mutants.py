@@ -23,6 +23,9 @@ MUTANTS = {
     10: "keys used as values in masked attention",
     11: "every head uses head 0's query",
     12: "masked attention scale applied twice",
+    13: "chunked form ignores key_start",
+    14: "chunked form reads key_start from the query's own row",
+    15: "chunked form reads the reserved word as mask bits",
 }
 
 
