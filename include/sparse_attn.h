@@ -170,11 +170,29 @@ int topk_bitmask_build(const int32_t* topk_idxs, const int32_t* q_lens, const in
  *                 128 keys); 32: one 32-bit word per 32 keys (control variant).
  *                 Both give bitwise-identical outputs.
  * Supported: (Dqk, Dv) = (192, 128). Requires padded_q >= Q, words % 4 == 0,
- * 32 * words >= KV; q, k, v, mask, out 16-byte aligned.
+ * words <= 2^22, 32 * words >= KV, KV <= 2^30; q, k, v, mask, out 16-byte aligned.
  */
 int masked_attn_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
                     int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
                     int64_t words, float scale, int mask_load_bits, void* stream);
+
+/*
+ * Chunked-context form (prhub summary of vLLM PR #48770, key source:
+ * offset_dense_mask_mod). k and v hold one chunk of KV keys of a longer
+ * context; chunk key j is key p = key_start[b] + j of the mask rows, where
+ * key_start[b] = mask[b][0][words-1] (the reserved word that
+ * topk_bitmask_build writes from key_starts), read as unsigned 32-bit:
+ *   J = { j < KV : p < 32 * (words - 1) and bit (p & 31) of mask[b][q][p >> 5] }
+ * Positions at or past the reserved word are never visible, so a start past
+ * every bit word gives o = 0. Otherwise as masked_attn_fwd: same arguments
+ * (no mask_load_bits: the words of a chunk tile sit at any bit offset and are
+ * read 4 bytes at a time), same layouts, no sink, o = 0 for an empty J.
+ * Requires mask != NULL (when B*Q*H > 0), words >= 4, words % 4 == 0,
+ * padded_q >= Q; KV is not limited by words. Returns SA_ERR_NULL without a mask.
+ */
+int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
+                           int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
+                           int64_t words, float scale, void* stream);
 
 #ifdef __cplusplus
 }

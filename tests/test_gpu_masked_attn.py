@@ -1,4 +1,5 @@
-"""masked_attn_fwd on the GPU against the CPU oracle, and the two forms against each other."""
+"""masked_attn_fwd / masked_attn_offset_fwd on the GPU against the CPU oracle, and the forms
+against each other. Masks that the oracle also reads are built by the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -11,11 +12,20 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _small(seed=31):
+def _small(seed=31, orc=None):
     inp = wl.masked_inputs("masked_small", seed, DEV)
     cfg = inp["config"]
-    mask = sa.topk_bitmask_build(inp["topk_idxs"], cfg.KV)
+    if orc is None:
+        mask = sa.topk_bitmask_build(inp["topk_idxs"], cfg.KV)
+    else:
+        mask = _oracle_mask(orc, inp["topk_idxs"], cfg.KV)
     return inp, cfg, mask
+
+
+def _oracle_mask(orc, idx, key_len, key_starts=None):
+    ks = None if key_starts is None else np.asarray(key_starts, dtype=np.int32)
+    m = orc.topk_mask_build(idx.cpu().numpy(), key_len, key_starts=ks)
+    return torch.from_numpy(m.view(np.int32)).to(DEV)
 
 
 def _ref(orc, inp, mask, rows=None):
@@ -25,7 +35,7 @@ def _ref(orc, inp, mask, rows=None):
 
 @pytest.mark.parametrize("bits_", [128, 32])
 def test_small_topk_mask(oracle_impl, bits_):
-    inp, cfg, mask = _small()
+    inp, cfg, mask = _small(orc=oracle_impl)
     out = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"], mask_load_bits=bits_)
     torch.cuda.synchronize()
     ref = _ref(oracle_impl, inp, mask).reshape(cfg.B, cfg.Q, cfg.H, cfg.Dv)
@@ -33,7 +43,7 @@ def test_small_topk_mask(oracle_impl, bits_):
 
 
 def test_small_dense_and_null_mask(oracle_impl):
-    inp, cfg, _ = _small(32)
+    inp, cfg, _ = _small(32, orc=oracle_impl)
     B, pq, W = sa.topk_bitmask_shape(cfg.B, cfg.Q, cfg.KV)
     ones = torch.full((B, pq, W), -1, dtype=torch.int32, device=DEV)
     a = sa.masked_attn(inp["q"], inp["k"], inp["v"], ones, inp["scale"])
@@ -88,7 +98,7 @@ def test_two_forms_agree(oracle_impl):
 def test_masked_config_sampled(oracle_impl):
     inp = wl.masked_inputs("masked", 1004, DEV)
     cfg = inp["config"]
-    mask = sa.topk_bitmask_build(inp["topk_idxs"], cfg.KV)
+    mask = _oracle_mask(oracle_impl, inp["topk_idxs"], cfg.KV)
     out = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"])
     out32 = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"], mask_load_bits=32)
     torch.cuda.synchronize()
@@ -97,3 +107,90 @@ def test_masked_config_sampled(oracle_impl):
     ref = _ref(oracle_impl, inp, mask, rows)
     got = to64(out.reshape(cfg.B * cfg.Q, cfg.H, cfg.Dv)[torch.as_tensor(rows, device=DEV)])
     assert_close(got, ref, "masked config")
+
+
+# --------------------------------------------------------------------------- chunked-context (offset) form
+def _chunk(inp, start, n, seed):
+    """k, v of a chunk of n keys (fresh values: the chunk is any slice of a longer context)."""
+    g = torch.Generator().manual_seed(seed)
+    B, _, H, Dqk = inp["q"].shape
+    Dv = inp["v"].shape[3]
+    k = torch.randn(B, n, H, Dqk, generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn(B, n, H, Dv, generator=g).to(torch.bfloat16).to(DEV)
+    return k, v
+
+
+def _offset_ref(orc, inp, k, v, mask, rows=None):
+    return orc.masked_attn_offset(bits(inp["q"]), bits(k), bits(v), mask.cpu().numpy().view(np.uint32), inp["scale"],
+                                  rows)
+
+
+@pytest.mark.parametrize("starts,n", [((0, 37), 130), ((96, 170), 64), ((250, 3), 130), ((31, 33), 1)],
+                         ids=["s0-37", "s96-170", "past-reserved", "one-key"])
+def test_offset_small_vs_oracle(oracle_impl, starts, n):
+    """Global context of 300 keys (12 words, the last reserved), chunk of n keys at per-batch
+    starts; (250, .) runs past the reserved word's position (352) and must see nothing there."""
+    inp, cfg, _ = _small(51)
+    mask = _oracle_mask(oracle_impl, inp["topk_idxs"], cfg.KV, key_starts=starts)
+    assert mask.shape[2] == 12
+    k, v = _chunk(inp, 0, n, 52)
+    out = sa.masked_attn_offset(inp["q"], k, v, mask, inp["scale"])
+    torch.cuda.synchronize()
+    ref = _offset_ref(oracle_impl, inp, k, v, mask).reshape(cfg.B, cfg.Q, cfg.H, cfg.Dv)
+    assert_close(to64(out), ref, f"offset {starts} n={n}")
+
+
+def test_offset_start_zero_equals_plain():
+    """Start 0 over the whole context: the same visible keys as the plain form, so the same
+    arithmetic and bitwise-identical outputs."""
+    inp, cfg, _ = _small(53)
+    B = cfg.B
+    mask = sa.topk_bitmask_build(inp["topk_idxs"], cfg.KV,
+                                 key_starts=torch.zeros(B, dtype=torch.int32, device=DEV))
+    a = sa.masked_attn_offset(inp["q"], inp["k"], inp["v"], mask, inp["scale"])
+    b = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("start", [37, 64, 200])
+def test_offset_equals_plain_on_shifted_mask(start):
+    """A chunk [start, start + n) read through the global mask's offset equals the plain form
+    over a mask built from the indices shifted by -start (bitwise: same keys, same arithmetic)."""
+    inp, cfg, _ = _small(54)
+    B, n = cfg.B, 90
+    starts = torch.full((B,), start, dtype=torch.int32, device=DEV)
+    gmask = sa.topk_bitmask_build(inp["topk_idxs"], cfg.KV, key_starts=starts)
+    k, v = _chunk(inp, start, n, 55)
+    a = sa.masked_attn_offset(inp["q"], k, v, gmask, inp["scale"])
+    shifted = inp["topk_idxs"] - start  # keys outside [0, n) are dropped by the builder
+    lmask = sa.topk_bitmask_build(shifted, n)
+    b = sa.masked_attn(inp["q"], k, v, lmask, inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_offset_start_past_context_is_zero():
+    inp, cfg, _ = _small(56)
+    starts = torch.tensor([5000, 352], dtype=torch.int32, device=DEV)  # 352 = first reserved position
+    mask = sa.topk_bitmask_build(inp["topk_idxs"], cfg.KV, key_starts=starts)
+    k, v = _chunk(inp, 0, 100, 57)
+    out = sa.masked_attn_offset(inp["q"], k, v, mask, inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_offset_masked_config_sampled(oracle_impl):
+    """The masked config's queries and mask (8192-key context) with a 4096-key chunk at starts
+    1000 and 2500 (neither a multiple of 32); sampled rows against the oracle."""
+    inp = wl.masked_inputs("masked", 1005, DEV)
+    cfg = inp["config"]
+    starts = (1000, 2500)
+    mask = _oracle_mask(oracle_impl, inp["topk_idxs"], cfg.KV, key_starts=starts)
+    k, v = _chunk(inp, 0, 4096, 58)
+    out = sa.masked_attn_offset(inp["q"], k, v, mask, inp["scale"])
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 1000, 2047, 2048, 2049, 3000, 4095])
+    ref = _offset_ref(oracle_impl, inp, k, v, mask, rows)
+    got = to64(out.reshape(cfg.B * cfg.Q, cfg.H, cfg.Dv)[torch.as_tensor(rows, device=DEV)])
+    assert_close(got, ref, "offset masked config")

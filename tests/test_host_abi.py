@@ -105,6 +105,22 @@ def test_masked_rejects_before_any_hip_call():
     assert _masked(Q=0) == 0
 
 
+def _offset(q=FAKE, k=FAKE, v=FAKE, m=FAKE, o=FAKE, B=1, Q=4, KV=64, H=2, Dqk=192, Dv=128, pq=128, W=8):
+    return _lib().masked_attn_offset_fwd(q, k, v, m, o, B, Q, KV, H, Dqk, Dv, pq, W, 0.1, None)
+
+
+def test_masked_offset_rejects_before_any_hip_call():
+    assert _offset(m=None) == 1      # the mask carries key_start
+    assert _offset(W=0) == 2         # no reserved word
+    assert _offset(W=6) == 2         # rows are whole 16-byte chunks
+    assert _offset(pq=2) == 2
+    assert _offset(Dqk=128) == 4
+    assert _offset(o=None) == 1
+    assert _offset(v=FAKE_ODD) == 3
+    assert _offset(m=FAKE_ODD) == 3
+    assert _offset(H=0) == 0
+
+
 def test_status_strings():
     for s in range(7):
         assert _lib().sa_status_string(s)

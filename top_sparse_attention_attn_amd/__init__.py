@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     SparseAttnError,
     library_path,
     masked_attn,
+    masked_attn_offset,
     new_workspace,
     sparse_attn,
     sparse_attn_merge,

@@ -23,7 +23,7 @@ SA_STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_ALIGN",
 
 EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_fwd",
             "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "topk_bitmask_shape", "topk_bitmask_build",
-            "masked_attn_fwd"]
+            "masked_attn_fwd", "masked_attn_offset_fwd"]
 
 
 class SparseAttnError(RuntimeError):
@@ -61,6 +61,8 @@ def _load():
         lib.topk_bitmask_build.restype = I
         lib.masked_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, F, I, P]
         lib.masked_attn_fwd.restype = I
+        lib.masked_attn_offset_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, F, P]
+        lib.masked_attn_offset_fwd.restype = I
         _lib = lib
         return lib
 
@@ -214,6 +216,20 @@ def masked_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.T
 
     q [B,Q,H,192], k [B,KV,H,192], v [B,KV,H,128] bf16; mask [B,padded_q,words] int32/uint32 bits.
     """
+    return _masked_call("masked_attn_fwd", q, k, v, mask, scale, out, (int(mask_load_bits),))
+
+
+def masked_attn_offset(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor, scale: float,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """Chunked-context form: k, v are a chunk of KV keys and chunk key j reads mask bit
+    key_start + j, with key_start = mask[b, 0, words-1] (written by topk_bitmask_build from
+    key_starts). Shapes as masked_attn; the mask is required."""
+    if mask is None:
+        raise ValueError("masked_attn_offset needs the mask (it carries key_start)")
+    return _masked_call("masked_attn_offset_fwd", q, k, v, mask, scale, out, ())
+
+
+def _masked_call(entry, q, k, v, mask, scale, out, extra):
     dev = q.device
     _check(q, "q", torch.bfloat16)
     _check(k, "k", torch.bfloat16, dev)
@@ -232,6 +248,6 @@ def masked_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.T
         out = torch.empty((B, Q, H, Dv), dtype=torch.bfloat16, device=dev)
     else:
         _check(out, "out", torch.bfloat16, dev)
-    _call("masked_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out), B, Q, KV, H, Dqk, Dv, padded_q, words,
-          float(scale), int(mask_load_bits), _stream_ptr(dev))
+    _call(entry, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out), B, Q, KV, H, Dqk, Dv, padded_q, words,
+          float(scale), *extra, _stream_ptr(dev))
     return out

@@ -18,7 +18,7 @@ int sa_internal_launch_bitmask(const int32_t* idx, const int32_t* q_lens, const 
 int64_t sa_internal_bitmask_max_words(void);
 int sa_internal_launch_masked(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
                               int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
-                              int64_t words, float scale, int mask_load_bits, void* stream);
+                              int64_t words, float scale, int mask_load_bits, int offset, void* stream);
 }
 
 namespace {
@@ -71,6 +71,22 @@ static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink
   const int rc = sa_internal_launch_sparse(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, nsplit,
                                            need > 0 ? workspace : nullptr, phases, stream);
   return rc == 0 ? SA_OK : SA_ERR_HIP;
+}
+
+int masked_run(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, int64_t B, int64_t Q,
+               int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q, int64_t words, float scale,
+               int mask_load_bits, int offset, void* stream) {
+  if (B < 0 || Q < 0 || KV < 0 || H < 0 || Dqk < 0 || Dv < 0 || padded_q < 0 || words < 0) return SA_ERR_SHAPE;
+  if (B * Q * H == 0) return SA_OK;
+  if (Dqk != 192 || Dv != 128) return SA_ERR_UNSUPPORTED;
+  if (mask && (padded_q < Q || words % 4 != 0 || words > ((int64_t)1 << 22))) return SA_ERR_SHAPE;
+  if (B * H * cdiv(Q, 128) > ((int64_t)1 << 31) - 1 || KV > ((int64_t)1 << 30)) return SA_ERR_SHAPE;
+  if (!q || !out || (KV > 0 && (!k || !v))) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (k && !aligned16(k)) || (v && !aligned16(v)) || (mask && !aligned16(mask)))
+    return SA_ERR_ALIGN;
+  const int rc = sa_internal_launch_masked(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale,
+                                           mask_load_bits, offset, stream);
+  return rc == 0 ? SA_OK : (rc == 2 ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
 }
 
 }  // namespace
@@ -156,18 +172,18 @@ int topk_bitmask_build(const int32_t* topk_idxs, const int32_t* q_lens, const in
 int masked_attn_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, int64_t B,
                     int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q, int64_t words,
                     float scale, int mask_load_bits, void* stream) {
-  if (B < 0 || Q < 0 || KV < 0 || H < 0 || Dqk < 0 || Dv < 0 || padded_q < 0 || words < 0) return SA_ERR_SHAPE;
   if (mask_load_bits != 128 && mask_load_bits != 32) return SA_ERR_SHAPE;
-  if (B * Q * H == 0) return SA_OK;
-  if (Dqk != 192 || Dv != 128) return SA_ERR_UNSUPPORTED;
-  if (mask && (padded_q < Q || words % 4 != 0 || 32 * words < KV)) return SA_ERR_SHAPE;
-  if (B * H * cdiv(Q, 128) > ((int64_t)1 << 31) - 1 || KV > ((int64_t)1 << 30)) return SA_ERR_SHAPE;
-  if (!q || !out || (KV > 0 && (!k || !v))) return SA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || (k && !aligned16(k)) || (v && !aligned16(v)) || (mask && !aligned16(mask)))
-    return SA_ERR_ALIGN;
-  const int rc = sa_internal_launch_masked(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale,
-                                           mask_load_bits, stream);
-  return rc == 0 ? SA_OK : (rc == 2 ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
+  if (mask && KV > 32 * words) return SA_ERR_SHAPE;
+  return masked_run(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale, mask_load_bits, 0, stream);
+}
+
+int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, int64_t B,
+                           int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
+                           int64_t words, float scale, void* stream) {
+  if (words < 0) return SA_ERR_SHAPE;
+  if (B * Q * H > 0 && !mask) return SA_ERR_NULL;
+  if (B * Q * H > 0 && words < 4) return SA_ERR_SHAPE;
+  return masked_run(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale, 128, 1, stream);
 }
 
 }  // extern "C"

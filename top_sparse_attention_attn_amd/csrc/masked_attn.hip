@@ -5,6 +5,12 @@
 // to the values; the mask row (b, q) is shared by all heads; no sink. The mask is read
 // four words (128 keys) per query and 16-byte load; a 4-byte-load variant exists only as
 // the control for measuring what the wide load saves, and gives identical results.
+// Chunked-context form (offset_dense_mask_mod in the PR #48770 summary): k and v are one
+// chunk of a longer context, and chunk key j is mask key key_start + j, key_start being the
+// reserved last word of query row 0 of the batch; keys at or past that word are not
+// visible. A chunk tile then straddles up to three mask words at any bit offset: the value
+// waves copy three words per query with 4-byte loads and the score waves funnel-shift them
+// (v_alignbit) into the tile's 64 bits.
 //
 // Decomposition: one workgroup of 8 waves per (batch, head, 128 queries), in two roles that
 // run one 64-key tile apart, as in the sparse kernel:
@@ -55,7 +61,7 @@ struct Smem {
 
 }  // namespace masked
 
-template <int DQK, int DV, int MASKBITS>
+template <int DQK, int DV, int MASKBITS, bool OFFSET>
 __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const uint32_t* __restrict__ mask, __bf16* __restrict__ out, int Q, int KV, int H, int padded_q, int words,
@@ -83,6 +89,14 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   const int h = bh % H, b = bh / H;
   const int qbase = qt * kQT + pw * 32;  // first query of this wave's group
   const int nkt = (KV + kKT - 1) / kKT;
+
+  // chunked-context form: the clamped start and the first position past the bit words
+  uint32_t ksc = 0, pmax = 0;
+  if constexpr (OFFSET) {
+    pmax = 32u * (uint32_t)(words - 1);
+    const uint32_t ks = mask[(size_t)b * padded_q * words + (words - 1)];
+    ksc = ks < pmax ? ks : pmax;
+  }
 
   // ---- score waves: queries (B operand), mask rows, softmax state
   bf16x8 qreg[2][DSTEPS];
@@ -144,13 +158,21 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   // Mask copy by the value waves, for tile t: the wide form copies the 4 words of keys
   // [128 c, 128 c + 128) of all kQT queries at the even tile t = 2c (two 16-byte loads, by waves
   // 4 and 5), into sm.mw[c & 1][query][4]; the control form copies the 2 words of tile t (four
-  // 4-byte loads, by waves 4-7) into sm.mw[t & 1][query][2]. Rows past padded_q read nothing.
+  // 4-byte loads, by waves 4-7) into sm.mw[t & 1][query][2]; the chunked form copies words
+  // w0 .. w0 + 3 of mask position 64 t + key_start (eight 4-byte loads) into
+  // sm.mw[t & 1][query][4]. Rows past padded_q read nothing.
   const int q0 = qt * kQT;
   auto mask_copy = [&](int t) {
     if (mask == nullptr) return;
     const u32x4 mr = buffer_rsrc(mask + ((size_t)b * padded_q + q0) * words,
                                  (uint32_t)(min(kQT, padded_q - q0) * words * 4));
-    if constexpr (MASKBITS == 128) {
+    if constexpr (OFFSET) {
+      const uint32_t w0 = (64u * (uint32_t)t + ksc) >> 5;
+      for (int i = pw; i < 8; i += 4) {
+        const int d = 64 * i + lane, ql = d >> 2;
+        dma_lds4(mr, (uint32_t)(ql * words + (int)w0 + (d & 3)) * 4u, lds_addr(sm.mw[t & 1]) + 256 * i);
+      }
+    } else if constexpr (MASKBITS == 128) {
       if ((t & 1) == 0 && pw < 2) {
         const int ql = 64 * pw + lane;
         dma_lds16(mr, (uint32_t)(ql * words * 4 + (t >> 1) * 16), lds_addr(sm.mw[(t >> 1) & 1]) + 1024 * pw);
@@ -214,7 +236,16 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) {
         const int ql = pw * 32 + 16 * qb + l16;
-        if (mask == nullptr) {
+        if constexpr (OFFSET) {
+          // bits of positions p0 .. p0 + 63, none at or past pmax
+          const uint4 x = *(const uint4*)&sm.mw[t & 1][ql * 4];
+          const uint32_t p0 = 64u * (uint32_t)t + ksc, sh = p0 & 31u;
+          const int rem = (int)pmax - (int)p0;
+          const uint32_t lim0 = rem >= 32 ? ~0u : (rem > 0 ? (1u << rem) - 1u : 0u);
+          const uint32_t lim1 = rem >= 64 ? ~0u : (rem > 32 ? (1u << (rem - 32)) - 1u : 0u);
+          mwd[qb][0] = qlive[qb] ? __builtin_amdgcn_alignbit(x.y, x.x, sh) & lim0 : 0u;
+          mwd[qb][1] = qlive[qb] ? __builtin_amdgcn_alignbit(x.z, x.y, sh) & lim1 : 0u;
+        } else if (mask == nullptr) {
           mwd[qb][0] = mwd[qb][1] = qlive[qb] ? ~0u : 0u;
         } else {
           const uint2 x = MASKBITS == 128 ? *(const uint2*)&sm.mw[(t >> 1) & 1][ql * 4 + 2 * (t & 1)]
@@ -380,20 +411,23 @@ static int masked_device_xccs() {
 
 extern "C" int sa_internal_launch_masked(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
                                          int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv,
-                                         int64_t padded_q, int64_t words, float scale, int mask_load_bits,
+                                         int64_t padded_q, int64_t words, float scale, int mask_load_bits, int offset,
                                          void* stream) {
   const int64_t nqt = (Q + sa::masked::kQT - 1) / sa::masked::kQT;
   const dim3 grid((unsigned)(B * H * nqt));
   const float sl2 = scale * sa::kLog2e;
   if (Dqk != 192 || Dv != 128) return 2;
   const int nxcc = sa::masked_device_xccs();
-  if (mask_load_bits == 32)
-    hipLaunchKernelGGL((sa::masked_attn_kernel<192, 128, 32>), grid, dim3(sa::masked::kThreads), 0,
-                       (hipStream_t)stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, mask, (__bf16*)out,
-                       (int)Q, (int)KV, (int)H, (int)padded_q, (int)words, nxcc, sl2);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(sa::masked::kThreads), 0, (hipStream_t)stream, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, mask, (__bf16*)out, (int)Q, (int)KV, (int)H, (int)padded_q,
+                       (int)words, nxcc, sl2);
+  };
+  if (offset)
+    launch(sa::masked_attn_kernel<192, 128, 128, true>);
+  else if (mask_load_bits == 32)
+    launch(sa::masked_attn_kernel<192, 128, 32, false>);
   else
-    hipLaunchKernelGGL((sa::masked_attn_kernel<192, 128, 128>), grid, dim3(sa::masked::kThreads), 0,
-                       (hipStream_t)stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, mask, (__bf16*)out,
-                       (int)Q, (int)KV, (int)H, (int)padded_q, (int)words, nxcc, sl2);
+    launch(sa::masked_attn_kernel<192, 128, 128, false>);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
