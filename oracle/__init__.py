@@ -17,6 +17,7 @@ Sources, per function:
   masked_attn          prhub summary of vLLM PR #48770 (masked-MHA path) and PR #52217
   masked_attn_offset   prhub summary of vLLM PR #48770, key source (offset_dense_mask_mod:
                        chunked context, key index + key_start from the reserved word)
+  candidate_mask       prhub summary of vLLM PR #56628 (the indexer's candidate-mask rule)
 """
 from __future__ import annotations
 
@@ -64,6 +65,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_masked_attn.restype = ctypes.c_int
     lib.oracle_masked_attn_offset.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, ctypes.c_double, P, I]
     lib.oracle_masked_attn_offset.restype = ctypes.c_int
+    lib.oracle_candidate_mask.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I]
+    lib.oracle_candidate_mask.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -188,6 +191,29 @@ class Oracle:
             B, Q, KV, H, Dqk, Dv, padded_q, W, float(scale), self._ptr(rows), len(rows))
         if rc != 0:
             raise ValueError("masked_attn oracle rejected its arguments")
+        return out
+
+
+    def candidate_mask(self, logits, ends, flags, block_size, starts=None, row_repeat=1) -> np.ndarray:
+        """The whole-row candidate mask applied to a copy of ``logits`` (float32 [rows, width], any
+        element strides that are multiples of 4 bytes). ends / starts int32 1-D (strided views
+        allowed), flags uint8 [rows, nblocks + 1]. Returns the masked copy."""
+        out = np.array(logits, dtype=np.float32, copy=True)
+        if out.ndim != 2:
+            raise ValueError("candidate_mask oracle: logits must be 2-D")
+        rows, width = out.shape
+        flags = np.ascontiguousarray(flags, dtype=np.uint8)
+        ends = np.asarray(ends)
+        if ends.dtype != np.int32 or (starts is not None and np.asarray(starts).dtype != np.int32):
+            raise ValueError("candidate_mask oracle: starts / ends must be int32")
+        st = None if starts is None else np.asarray(starts)
+        sr, sc = out.strides[0] // 4, out.strides[1] // 4
+        rc = self.lib.oracle_candidate_mask(
+            out.ctypes.data, None if st is None else st.ctypes.data, ends.ctypes.data, flags.ctypes.data,
+            rows, width, sr, sc, 0 if st is None else st.strides[0] // 4, ends.strides[0] // 4, int(block_size),
+            int(row_repeat))
+        if rc != 0:
+            raise ValueError("candidate_mask oracle rejected its arguments")
         return out
 
 

@@ -26,6 +26,10 @@
  *            prefill": key-source section (dense_mask_mod: word = kv >> 5,
  *            bit = kv & 31, LSB first; offset_dense_mask_mod reads key_start
  *            from the last word of query row 0 and adds it to the key index).
+ *  [PR56628] prhub summary of vLLM PR #56628 "ROCm DSA decode mask strides to
+ *            each row's end": the candidate-mask rule (live columns
+ *            [start, end), per-block keep flags relative to start, the edge
+ *            flag for the last column, -inf elsewhere) and its tests.
  *
  * Parity pins for every function here live in tests/test_oracle_pins.py.
  */
@@ -336,6 +340,54 @@ int oracle_masked_attn_offset(const uint16_t* q, const uint16_t* k, const uint16
                               double* out, int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv,
                               int64_t padded_q, int64_t W, double scale, const int64_t* rows, int64_t nrows) {
   return masked_attn_impl(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, W, scale, rows, nrows, 1);
+}
+
+/* ------------------------------------------------------------------------ */
+/* candidate mask  ([PR56628] the indexer's candidate-mask rule)            */
+/* ------------------------------------------------------------------------ */
+/*
+ * The rule of the shared whole-row kernel that the strided MI355X variant must
+ * match on [0, end) ([PR56628], key source: the strided kernel's mask rule and
+ * its tests' contract). logits [rows] x [width] float, element (r, c) at
+ * logits[r * stride_row + c * stride_col], modified in place. For row r, with
+ * i = r / row_repeat, s = starts ? starts[i * stride_start] : 0,
+ * e = ends[i * stride_end], nblocks = ceil(width / block_size):
+ *   column c is live iff s <= c < e;
+ *   a live column is kept iff flags[r][(c - s) / block_size] != 0 (a block
+ *   index outside [0, nblocks) keeps nothing) or c == width - 1 and the edge
+ *   flag flags[r][nblocks] != 0;
+ *   every column that is not kept, live or not, becomes -inf; kept columns are
+ *   left as they are.
+ * flags is uint8 [rows][nblocks + 1]. Returns 0, or -1 on a bad argument.
+ */
+int oracle_candidate_mask(float* logits, const int32_t* starts, const int32_t* ends, const uint8_t* flags,
+                          int64_t rows, int64_t width, int64_t stride_row, int64_t stride_col, int64_t stride_start,
+                          int64_t stride_end, int64_t block_size, int64_t row_repeat) {
+  if (!logits || !ends || !flags || rows < 0 || width < 0 || block_size < 1 || row_repeat < 1) return -1;
+  const int64_t nblocks = (width + block_size - 1) / block_size;
+  for (int64_t r = 0; r < rows; r++) {
+    const int64_t i = r / row_repeat;
+    const int64_t s = starts ? starts[i * stride_start] : 0;
+    const int64_t e = ends[i * stride_end];
+    const uint8_t* fr = flags + r * (nblocks + 1);
+    for (int64_t c = 0; c < width; c++) {
+      const int live = (s <= c) && (c < e);
+      int keep = 0;
+      if (live) {
+#if ORACLE_MUTANT == 16
+        const int64_t blk = c / block_size; /* mutant: block counted from column 0, not from the start */
+#else
+        const int64_t blk = (c - s) / block_size;
+#endif
+        if (blk >= 0 && blk < nblocks && fr[blk] != 0) keep = 1;
+#if ORACLE_MUTANT != 17
+        if (c == width - 1 && fr[nblocks] != 0) keep = 1; /* mutant 17: edge flag ignored */
+#endif
+      }
+      if (!keep) logits[r * stride_row + c * stride_col] = -INFINITY;
+    }
+  }
+  return 0;
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */

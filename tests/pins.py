@@ -8,8 +8,8 @@ tiny inputs. The checks are plain functions so that the mutation test can run
 them against deliberately broken builds of the oracle as well.
 
 Sources: "DeepSeek V4 源码剖析" ch. 5 (sections 5.1, 5.2, 5.4, 5.5); prhub
-summaries of vLLM PR #52217 (mask shape rule, worked example) and PR #48770
-(bit order, masked-MHA form).
+summaries of vLLM PR #52217 (mask shape rule, worked example), PR #48770
+(bit order, masked-MHA form) and PR #56628 (candidate-mask rule, its test ends).
 """
 from __future__ import annotations
 
@@ -475,6 +475,73 @@ def check_offset_stops_at_reserved_word(o):
     assert np.all(empty == 0.0)
 
 
+# --------------------------------------------------------------------------- candidate mask pins
+def _kept(row):
+    return np.flatnonzero(row != -np.inf)
+
+
+def check_candmask_closed_forms(o):
+    """All block flags set with start 0 and end = width keeps the row as it is; no flag at all
+    masks every column; an end <= 0 masks everything; an end past width acts as width; the edge
+    flag alone keeps exactly column width-1, and only when that column is live (end = width)."""
+    g = np.random.default_rng(31)
+    rows, width, bs = 6, 100, 16
+    nb = -(-width // bs)
+    x = g.standard_normal((rows, width)).astype(np.float32)
+    ends = np.array([width, width, 0, -5, width + 40, width - 1], dtype=np.int32)
+    flags = np.zeros((rows, nb + 1), dtype=np.uint8)
+    flags[0, :nb] = 1
+    flags[2, :] = 1
+    flags[3, :] = 1
+    flags[4, :nb] = 1
+    flags[5, nb] = 1
+    flags[1, nb] = 1
+    got = o.candidate_mask(x, ends, flags, bs)
+    assert np.array_equal(got[0], x[0])
+    assert np.array_equal(_kept(got[1]), [width - 1]) and got[1, width - 1] == x[1, width - 1]
+    assert not np.isfinite(got[2]).any() and not np.isfinite(got[3]).any()
+    assert np.array_equal(got[4], x[4])
+    assert len(_kept(got[5])) == 0  # end = width - 1: column width-1 is not live
+
+
+def check_candmask_single_block(o):
+    """One block flag b with start s keeps exactly columns [s + b*bs, min(s + (b+1)*bs, e)):
+    blocks are counted from the row's start, not from column 0."""
+    g = np.random.default_rng(32)
+    width, bs = 200, 8
+    nb = -(-width // bs)
+    cases = [(0, 200, 3), (13, 200, 0), (13, 40, 3), (50, 150, 11), (7, 190, 22)]
+    x = g.standard_normal((len(cases), width)).astype(np.float32)
+    starts = np.array([c[0] for c in cases], dtype=np.int32)
+    ends = np.array([c[1] for c in cases], dtype=np.int32)
+    flags = np.zeros((len(cases), nb + 1), dtype=np.uint8)
+    for r, (_, _, b) in enumerate(cases):
+        flags[r, b] = 1
+    got = o.candidate_mask(x, ends, flags, bs, starts=starts)
+    for r, (st, en, b) in enumerate(cases):
+        lo, hi = st + b * bs, min(st + (b + 1) * bs, en)
+        assert np.array_equal(_kept(got[r]), np.arange(lo, max(lo, hi))), (r, _kept(got[r]))
+        assert np.array_equal(got[r, lo:hi], x[r, lo:hi])
+
+
+def check_candmask_row_repeat_and_page_ends(o):
+    """With every flag set, row r keeps exactly [0, e) for the page's test ends (0, 1, the
+    1024-column tile edges, width-1, width, width/2); with row_repeat 2, rows 2i and 2i+1 share
+    ends[i]."""
+    width = 4096
+    ends_list = [0, 1, 1023, 1024, 1025, width - 1, width, width // 2]
+    rows = len(ends_list)
+    x = np.ones((rows, width), dtype=np.float32)
+    flags = np.ones((rows, width // 16 + 1), dtype=np.uint8)
+    got = o.candidate_mask(x, np.array(ends_list, dtype=np.int32), flags, 16)
+    for r, e in enumerate(ends_list):
+        assert np.array_equal(_kept(got[r]), np.arange(e)), r
+    half = np.array(ends_list[::2], dtype=np.int32)
+    got2 = o.candidate_mask(x, half, flags, 16, row_repeat=2)
+    for r in range(rows):
+        assert np.array_equal(_kept(got2[r]), np.arange(half[r // 2])), r
+
+
 SPARSE_PINS = [check_loop_semantics, check_all_invalid_zero, check_order_invariance, check_dense_equivalence,
                check_sink_extra_key, check_exact_mean, check_sink_halves, check_single_row, check_inf_nan_sink,
                check_huge_sink, check_duplicates_count, check_scale_closed_form, check_out_of_range_is_empty]
@@ -482,4 +549,5 @@ MASK_PINS = [check_mask_worked_example, check_mask_brute_force, check_mask_singl
              check_mask_reserved_word]
 MASKED_PINS = [check_masked_dense, check_masked_random, check_two_forms_agree, check_offset_chunk_is_sdpa,
                check_offset_zero_start_is_plain, check_offset_stops_at_reserved_word]
-ALL_PINS = SPARSE_PINS + MASK_PINS + MASKED_PINS
+CANDIDATE_PINS = [check_candmask_closed_forms, check_candmask_single_block, check_candmask_row_repeat_and_page_ends]
+ALL_PINS = SPARSE_PINS + MASK_PINS + MASKED_PINS + CANDIDATE_PINS

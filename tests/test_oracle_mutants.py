@@ -26,6 +26,8 @@ MUTANTS = {
     13: "chunked form ignores key_start",
     14: "chunked form reads key_start from the query's own row",
     15: "chunked form reads the reserved word as mask bits",
+    16: "candidate blocks counted from column 0 instead of the start",
+    17: "candidate edge flag ignored",
 }
 
 
