@@ -1,6 +1,7 @@
 """Throughput of top-k sparse attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|prefill|ragged|masked|bitmask]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--config decode|prefill|ragged|masked|bitmask|candidate|candidate_long]
 
 One step is one pass of the hot path over one batch of synthetic input that is
 already resident in HBM. The default workload is the decode shape B=64, S=1,
@@ -37,7 +38,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", choices=["decode", "prefill", "ragged", "masked", "bitmask", "tiny"])
+    p.add_argument("--config", default="decode", choices=["decode", "prefill", "ragged", "masked", "bitmask", "tiny", "candidate",
+                                                        "candidate_long"])
     p.add_argument("--sets", type=int, default=NSETS)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -95,6 +97,28 @@ def masked_work(inp, mask_bytes: int) -> tuple[float, float]:
     nbytes = (c.B * c.Q * c.H * c.Dqk + c.B * c.KV * c.H * (c.Dqk + c.Dv) + c.B * c.Q * c.H * c.Dv) * 2 + mask_bytes
     flops = 2.0 * c.B * c.H * c.Q * c.KV * (c.Dqk + c.Dv)
     return float(nbytes), flops
+
+
+def candidate_work(inp) -> float:
+    """Algorithmic bytes of one candidate-mask call: a flag byte per live block and the edge
+    flag, the end, and a 4-byte -inf store per live column that is not kept (starts are 0)."""
+    ends = inp["ends"].cpu().numpy().astype(np.int64)
+    flags = inp["flags"].cpu().numpy()
+    cfg = inp["config"]
+    bs, width = cfg.block_size, cfg.width
+    total = 0
+    for r in range(cfg.rows):
+        lim = max(0, min(int(ends[r]), width))
+        nb = -(-lim // bs)
+        kept_blocks = flags[r, :nb].astype(bool)
+        sizes = np.full(nb, bs, dtype=np.int64)
+        if nb:
+            sizes[-1] = lim - (nb - 1) * bs
+        kept = int(sizes[kept_blocks].sum())
+        if lim == width and flags[r, -1] and not (nb and kept_blocks[-1]):
+            kept += 1  # the edge column
+        total += 4 * (lim - kept) + nb + 1 + 4
+    return float(total)
 
 
 def cpu_baseline(args, make_call_inputs, unit_per_call: float, unit: str, sample_desc: str):
@@ -174,6 +198,32 @@ def main():
             return (lambda: orc.sparse_attn(qb, kvb, sk, ix, x["scale"], toks)), len(toks)
 
         sample_desc = ("all tokens of one step" if args.config != "prefill" else "every 64th token of one step")
+    elif args.config in ("candidate", "candidate_long"):
+        cfg = wl.CANDIDATE_CONFIGS[args.config]
+        nsets = min(args.sets, 2)  # 402 MB of logits per set
+        sets = [wl.candidate_inputs(cfg, 2001 + i, dev) for i in range(nsets)]
+
+        def step(i):
+            x = sets[i % nsets]
+            sa.candidate_mask_apply(x["logits"], x["ends"], x["flags"], x["block_size"])
+
+        kernel_step, kernel_name = step, "candidate_mask_kernel<false>"
+        work = [(candidate_work(x), 0.0, candidate_work(x)) for x in sets]
+        units_per_step = cfg.rows
+        unit = "decode rows/s"
+        bound = "hbm"
+        workload = (f"candidate_mask rows={cfg.rows} width={cfg.width} block={cfg.block_size}, "
+                    f"ends ~ U[{cfg.end_lo}, {cfg.end_hi}], flags kept with p = 0.5")
+        extra_cfg = {"rows": cfg.rows, "width": cfg.width, "block_size": cfg.block_size,
+                     "grid": sa.candidate_mask_grid(cfg.rows, cfg.width)}
+
+        def make_cpu(orc):
+            x = sets[0]
+            lg = x["logits"].cpu().numpy()
+            en, fl = x["ends"].cpu().numpy(), x["flags"].cpu().numpy()
+            return (lambda: orc.candidate_mask(lg, en, fl, cfg.block_size)), cfg.rows
+
+        sample_desc = "all rows of one step, whole-row rule over the full width"
     else:
         cfg = wl.MASKED_CONFIGS["masked"]
         nsets = min(args.sets, 4)
@@ -197,7 +247,7 @@ def main():
             def make_cpu(orc):
                 x = sets[0]
                 qb, kb, vb = oracle_bits(x["q"]), oracle_bits(x["k"]), oracle_bits(x["v"])
-                m = masks[0].cpu().numpy().view(np.uint32)
+                m = orc.topk_mask_build(x["topk_idxs"].cpu().numpy(), cfg.KV)
                 rows = np.arange(0, cfg.B * cfg.Q, 64)
                 return (lambda: orc.masked_attn(qb, kb, vb, m, x["scale"], rows)), len(rows)
 
@@ -281,7 +331,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.config != "bitmask" else "int32",
+        "dtype": {"bitmask": "int32", "candidate": "f32", "candidate_long": "f32"}.get(args.config, "bf16"),
         "data": "synthetic",
         "config": {"workload": workload, **extra_cfg},
         "roofline": roof,

@@ -194,6 +194,45 @@ int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const ui
                            int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
                            int64_t words, float scale, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Candidate mask of the indexer's decode logits.                           */
+/* prhub summary of vLLM PR #56628 (ROCm DSA decode: the candidate mask      */
+/* strides only up to each row's live end; the mask rule and the tests'      */
+/* contract: agreement on [0, end), columns past it untouched, the launch     */
+/* grid fixed by the shapes so graph replay follows changing ends).          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * logits  device float32; element (r, c) at logits[r * stride_row + c * stride_col]
+ *         (0 <= r < rows, 0 <= c < width), modified in place.
+ * starts  device int32 or NULL (NULL: every start is 0); row r uses
+ *         starts[(r / row_repeat) * stride_start].
+ * ends    device int32; row r uses e = ends[(r / row_repeat) * stride_end].
+ * flags   device uint8 [rows][nblocks + 1], nblocks = ceil(width / block_size):
+ *         flags[r][b] != 0 keeps block b of row r, the columns
+ *         start + b * block_size ... start + (b + 1) * block_size - 1;
+ *         flags[r][nblocks] != 0 (the edge flag) keeps column width - 1.
+ *         How the flags are derived from candidate blocks is not printed on
+ *         the page; they are an input here.
+ * For each row, a column c with start <= c < e is live; a live column keeps
+ * its value iff its block flag is set (a block index outside [0, nblocks)
+ * keeps nothing) or c == width - 1 and the edge flag is set. Every other
+ * column c < min(e, width) becomes -inf. Columns c >= e are NOT written (the
+ * whole-row form would set them to -inf too; no consumer reads them), so the
+ * cost follows the live length, not the workspace width. e <= 0 writes nothing.
+ * Launch: candidate_mask_grid(rows, width) workgroups, a function of the shapes
+ * only, so a captured graph replays correctly with new starts / ends / flags.
+ * Requires block_size >= 1, row_repeat >= 1, stride_col >= 1, other strides
+ * >= 0, width < 2^31 - 4096; logits, starts, ends 4-byte aligned; ends (and
+ * starts) hold ceil(rows / row_repeat) entries.
+ */
+int candidate_mask_apply(float* logits, const int32_t* starts, const int32_t* ends, const uint8_t* flags,
+                         int64_t rows, int64_t width, int64_t stride_row, int64_t stride_col, int64_t stride_start,
+                         int64_t stride_end, int64_t block_size, int64_t row_repeat, void* stream);
+
+/* Host-only: the number of workgroups candidate_mask_apply launches (0 for no work). */
+int candidate_mask_grid(int64_t rows, int64_t width);
+
 #ifdef __cplusplus
 }
 #endif

@@ -121,6 +121,29 @@ def test_masked_offset_rejects_before_any_hip_call():
     assert _offset(H=0) == 0
 
 
+def _cand(lg=FAKE, st=None, en=FAKE, fl=FAKE, rows=4, width=1000, sr=1000, sc=1, ss=1, se=1, bs=16, rr=1):
+    return _lib().candidate_mask_apply(lg, st, en, fl, rows, width, sr, sc, ss, se, bs, rr, None)
+
+
+def test_candidate_mask_rejects_before_any_hip_call():
+    assert _cand(bs=0) == 2
+    assert _cand(rr=0) == 2
+    assert _cand(sc=0) == 2
+    assert _cand(sr=-1) == 2
+    assert _cand(width=1 << 31) == 2
+    assert _cand(en=None) == 1
+    assert _cand(fl=None) == 1
+    assert _cand(lg=ctypes.c_void_p((1 << 20) + 2)) == 3
+    assert _cand(rows=0) == 0 and _cand(width=0) == 0
+
+
+def test_candidate_grid_depends_on_shapes_only():
+    assert sa.candidate_mask_grid(96, 1 << 20) == 96 * (2048 // 96)
+    assert sa.candidate_mask_grid(1, 8192) == 8          # one workgroup per 1024-column tile at most
+    assert sa.candidate_mask_grid(4096, 1 << 20) == 4096  # at least one per row
+    assert sa.candidate_mask_grid(0, 100) == 0
+
+
 def test_status_strings():
     for s in range(7):
         assert _lib().sa_status_string(s)

@@ -8,6 +8,8 @@ unloadable library raises immediately (there is no fallback path).
 """
 from .api import (  # noqa: F401
     SparseAttnError,
+    candidate_mask_apply,
+    candidate_mask_grid,
     library_path,
     masked_attn,
     masked_attn_offset,

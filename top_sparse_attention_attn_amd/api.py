@@ -23,7 +23,7 @@ SA_STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_ALIGN",
 
 EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_fwd",
             "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "topk_bitmask_shape", "topk_bitmask_build",
-            "masked_attn_fwd", "masked_attn_offset_fwd"]
+            "masked_attn_fwd", "masked_attn_offset_fwd", "candidate_mask_apply", "candidate_mask_grid"]
 
 
 class SparseAttnError(RuntimeError):
@@ -63,6 +63,10 @@ def _load():
         lib.masked_attn_fwd.restype = I
         lib.masked_attn_offset_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, F, P]
         lib.masked_attn_offset_fwd.restype = I
+        lib.candidate_mask_apply.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P]
+        lib.candidate_mask_apply.restype = I
+        lib.candidate_mask_grid.argtypes = [I64, I64]
+        lib.candidate_mask_grid.restype = I
         _lib = lib
         return lib
 
@@ -86,6 +90,22 @@ def _check(t: torch.Tensor, name: str, dtype, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_strided(t: torch.Tensor, name: str, dtype, dim: int, device=None):
+    """Like _check, but any (non-negative) element strides are accepted."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D")
+    if any(st < 0 for st in t.stride()):
+        raise ValueError(f"{name} has a negative stride")
 
 
 def _call(fn_name: str, *args):
@@ -251,3 +271,43 @@ def _masked_call(entry, q, k, v, mask, scale, out, extra):
     _call(entry, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out), B, Q, KV, H, Dqk, Dv, padded_q, words,
           float(scale), *extra, _stream_ptr(dev))
     return out
+
+
+# --------------------------------------------------------------------------- candidate mask
+def candidate_mask_grid(rows: int, width: int) -> int:
+    """Workgroups candidate_mask_apply launches for these shapes (a function of the shapes only)."""
+    return int(_load().candidate_mask_grid(int(rows), int(width)))
+
+
+def candidate_mask_apply(logits: torch.Tensor, ends: torch.Tensor, flags: torch.Tensor, block_size: int,
+                         starts: torch.Tensor | None = None, row_repeat: int = 1) -> torch.Tensor:
+    """Mask the indexer's decode logits in place: for row r (sharing starts/ends with the other
+    rows of r // row_repeat), columns [start, end) keep their value where the block flag
+    flags[r, (c - start) // block_size] (or, for the last column, the edge flag flags[r, nblocks])
+    is set and become -inf otherwise; columns below start become -inf; columns at or past end
+    are left as they are.
+
+    logits float32 [rows, width] (any strides); ends / starts int32 1-D with ceil(rows /
+    row_repeat) entries (any stride); flags uint8 [rows, ceil(width / block_size) + 1] contiguous.
+    Returns logits.
+    """
+    dev = logits.device
+    _check_strided(logits, "logits", torch.float32, 2)
+    _check_strided(ends, "ends", torch.int32, 1, dev)
+    if starts is not None:
+        _check_strided(starts, "starts", torch.int32, 1, dev)
+    _check(flags, "flags", torch.uint8, dev)
+    rows, width = logits.shape
+    block_size, row_repeat = int(block_size), int(row_repeat)
+    if block_size < 1 or row_repeat < 1:
+        raise ValueError("block_size and row_repeat must be >= 1")
+    nb = -(-width // block_size)
+    if tuple(flags.shape) != (rows, nb + 1):
+        raise ValueError(f"flags must be [{rows}, {nb + 1}]")
+    need = -(-rows // row_repeat)
+    if ends.shape[0] < need or (starts is not None and starts.shape[0] < need):
+        raise ValueError(f"ends / starts need {need} entries")
+    _call("candidate_mask_apply", _ptr(logits), _ptr(starts), _ptr(ends), _ptr(flags), rows, width,
+          logits.stride(0), logits.stride(1), 0 if starts is None else starts.stride(0), ends.stride(0), block_size,
+          row_repeat, _stream_ptr(dev))
+    return logits

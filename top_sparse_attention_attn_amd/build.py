@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 LIBRARY = os.path.join(HERE, "libsparse_attn.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["sparse_attn.hip", "bitmask.hip", "masked_attn.hip", "capi.cpp"]
+SOURCES = ["sparse_attn.hip", "bitmask.hip", "masked_attn.hip", "candidate_mask.hip", "capi.cpp"]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -45,7 +45,7 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIBRARY + ".tmp"
     # --no-undefined: a kernel whose host stub was not emitted fails here, not at load time

@@ -19,6 +19,11 @@ int64_t sa_internal_bitmask_max_words(void);
 int sa_internal_launch_masked(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
                               int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
                               int64_t words, float scale, int mask_load_bits, int offset, void* stream);
+int sa_internal_candidate_gcols(int64_t rows, int64_t width);
+int sa_internal_launch_candidate_mask(float* logits, const int32_t* starts, const int32_t* ends, const uint8_t* flags,
+                                      int64_t rows, int64_t width, int64_t stride_row, int64_t stride_col,
+                                      int64_t stride_start, int64_t stride_end, int64_t block_size, int64_t row_repeat,
+                                      void* stream);
 }
 
 namespace {
@@ -184,6 +189,26 @@ int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const ui
   if (B * Q * H > 0 && !mask) return SA_ERR_NULL;
   if (B * Q * H > 0 && words < 4) return SA_ERR_SHAPE;
   return masked_run(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale, 128, 1, stream);
+}
+
+int candidate_mask_apply(float* logits, const int32_t* starts, const int32_t* ends, const uint8_t* flags,
+                         int64_t rows, int64_t width, int64_t stride_row, int64_t stride_col, int64_t stride_start,
+                         int64_t stride_end, int64_t block_size, int64_t row_repeat, void* stream) {
+  if (rows < 0 || width < 0 || block_size < 1 || row_repeat < 1) return SA_ERR_SHAPE;
+  if (stride_row < 0 || stride_col < 1 || stride_start < 0 || stride_end < 0) return SA_ERR_SHAPE;
+  if (rows == 0 || width == 0) return SA_OK;
+  if (width > ((int64_t)1 << 31) - 1 - 4096 || rows > ((int64_t)1 << 31) - 1) return SA_ERR_SHAPE;
+  if (rows * (int64_t)sa_internal_candidate_gcols(rows, width) > ((int64_t)1 << 31) - 1) return SA_ERR_SHAPE;
+  if (!logits || !ends || !flags) return SA_ERR_NULL;
+  if (((uintptr_t)logits & 3u) || ((uintptr_t)ends & 3u) || (starts && ((uintptr_t)starts & 3u))) return SA_ERR_ALIGN;
+  const int rc = sa_internal_launch_candidate_mask(logits, starts, ends, flags, rows, width, stride_row, stride_col,
+                                                   stride_start, stride_end, block_size, row_repeat, stream);
+  return rc == 0 ? SA_OK : SA_ERR_HIP;
+}
+
+int candidate_mask_grid(int64_t rows, int64_t width) {
+  if (rows <= 0 || width <= 0) return 0;
+  return (int)(rows * sa_internal_candidate_gcols(rows, width));
 }
 
 }  // extern "C"

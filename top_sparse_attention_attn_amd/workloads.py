@@ -62,6 +62,25 @@ MASKED_CONFIGS = {
 }
 
 
+@dataclass(frozen=True)
+class CandidateConfig:
+    name: str
+    rows: int          # decode rows (batch x next_n)
+    width: int         # logits workspace width (the engine's longest context)
+    block_size: int
+    end_lo: int        # live ends ~ U[end_lo, end_hi]
+    end_hi: int
+
+
+CANDIDATE_CONFIGS = {
+    # The indexer's decode logits at a 1M-token workspace with ~128 live columns per row and 96
+    # rows (the case the ROCm candidate-mask change was measured on), and a long-context mix.
+    "candidate": CandidateConfig("candidate", rows=96, width=1 << 20, block_size=16, end_lo=64, end_hi=192),
+    "candidate_long": CandidateConfig("candidate_long", rows=96, width=1 << 20, block_size=16, end_lo=0,
+                                      end_hi=1 << 20),
+}
+
+
 def _cpu_gen(seed: int) -> torch.Generator:
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
@@ -177,3 +196,17 @@ def masked_inputs(cfg: MaskedConfig | str, seed: int, device="cpu") -> dict:
     v = randn_bf16((cfg.B, cfg.KV, cfg.H, cfg.Dv), seed * 4 + 3, device)
     idx = topk_lists(cfg.B, cfg.Q, cfg.topk, cfg.KV, seed * 4 + 4).to(device)
     return {"q": q, "k": k, "v": v, "topk_idxs": idx, "scale": cfg.Dqk ** -0.5, "config": cfg, "seed": seed}
+
+
+def candidate_inputs(cfg: CandidateConfig | str, seed: int, device="cpu", keep_prob: float = 0.5) -> dict:
+    """logits [rows, width] fp32 N(0,1), ends ~ U[end_lo, end_hi] int32, random keep flags
+    [rows, nblocks + 1] uint8 (each block kept with keep_prob; the edge flag likewise)."""
+    if isinstance(cfg, str):
+        cfg = CANDIDATE_CONFIGS[cfg]
+    g = _cpu_gen(seed)
+    nb = -(-cfg.width // cfg.block_size)
+    ends = torch.randint(cfg.end_lo, cfg.end_hi + 1, (cfg.rows,), generator=g, dtype=torch.int64).to(torch.int32)
+    flags = (torch.rand((cfg.rows, nb + 1), generator=g) < keep_prob).to(torch.uint8)
+    logits = torch.randn((cfg.rows, cfg.width), generator=_dev_gen(seed * 3 + 1, device), device=device)
+    return {"logits": logits, "ends": ends.to(device), "flags": flags.to(device), "block_size": cfg.block_size,
+            "config": cfg, "seed": seed}
