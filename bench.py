@@ -1,7 +1,7 @@
 """Throughput of top-k sparse attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config decode|prefill|ragged|masked|bitmask|candidate|candidate_long]
+                    [--config decode|decode_fp8|prefill|ragged|masked|bitmask|candidate|candidate_long]
 
 One step is one pass of the hot path over one batch of synthetic input that is
 already resident in HBM. The default workload is the decode shape B=64, S=1,
@@ -38,8 +38,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", choices=["decode", "prefill", "ragged", "masked", "bitmask", "tiny", "candidate",
-                                                        "candidate_long"])
+    p.add_argument("--config", default="decode", choices=["decode", "decode_fp8", "prefill", "ragged", "masked", "bitmask", "tiny",
+                                                        "candidate", "candidate_long"])
     p.add_argument("--sets", type=int, default=NSETS)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -60,15 +60,16 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
 
 
-def sparse_work(inp, nsplit: int) -> tuple[float, float, float]:
+def sparse_work(inp, nsplit: int, row_bytes: int | None = None) -> tuple[float, float, float]:
     """Algorithmic bytes and flops of one sparse_attn call (gathered valid rows, q, o, indices),
     and the algorithmic bytes of its main kernel alone (the same without o when the call has
-    split partials, whose merge kernel writes o)."""
+    split partials, whose merge kernel writes o). row_bytes: bytes per gathered row (D*2 for
+    bf16 rows, 584 for FP8 rows)."""
     q, idx = inp["q"], inp["topk_idxs"]
     B, S, H, D = q.shape
     T = inp["kv"].shape[1]
     n_valid = int(((idx >= 0) & (idx < T)).sum().item())
-    nbytes = n_valid * D * 2 + 2 * B * S * H * D * 2 + idx.numel() * 4
+    nbytes = n_valid * (row_bytes or D * 2) + 2 * B * S * H * D * 2 + idx.numel() * 4
     flops = 4.0 * H * D * n_valid
     main_bytes = nbytes - (B * S * H * D * 2 if nsplit > 1 else 0)
     return float(nbytes), flops, float(main_bytes)
@@ -160,41 +161,56 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    if args.config in ("decode", "prefill", "ragged", "tiny"):
-        cfg = wl.SPARSE_CONFIGS[args.config]
+    if args.config in ("decode", "decode_fp8", "prefill", "ragged", "tiny"):
+        fp8 = args.config == "decode_fp8"
+        cfg = wl.SPARSE_CONFIGS["decode" if fp8 else args.config]
         nsets = args.sets if args.config != "ragged" else 1  # one ragged set is 8.6 GB of kv
         sets = [wl.sparse_inputs(cfg, 2001 + i, dev) for i in range(nsets)]
+        if fp8:  # the same queries and indices over FP8 rows (584 bytes each)
+            for i, x in enumerate(sets):
+                x["kv"] = wl.fp8_kv_rows(cfg.B, cfg.T, 3001 + i, dev)
         out = torch.empty_like(sets[0]["q"])
         ws_bytes = sa.sparse_attn_workspace_bytes(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)
         ws = sa.new_workspace(ws_bytes, dev)
 
         nsplit = sa.sparse_attn_num_splits(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)
 
+        attn = sa.sparse_attn_fp8 if fp8 else sa.sparse_attn
+
         def step(i):
             x = sets[i % nsets]
-            sa.sparse_attn(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
+            attn(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
 
         def kernel_step(i):  # the main kernel alone (the first of the call's two phases)
             x = sets[i % nsets]
             sa.sparse_attn_split(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
 
+        if fp8:  # no split-phase entry for FP8 rows: the whole call stands for the kernel
+            kernel_step = step
+
         hb = 1 if cfg.H <= 16 else (2 if cfg.H <= 32 else (4 if cfg.H <= 64 else 8))
-        kernel_name = f"sparse_attn_kernel<{cfg.D},{hb}>"
-        work = [sparse_work(x, nsplit) for x in sets]
+        kernel_name = f"sparse_attn_kernel<{cfg.D},{hb},fp8> + merge" if fp8 else f"sparse_attn_kernel<{cfg.D},{hb}>"
+        work = [sparse_work(x, nsplit, 584 if fp8 else None) for x in sets]
+        if fp8:  # the whole call is timed as the kernel: count its output too
+            work = [(w[0], w[1], w[0]) for w in work]
         units_per_step = cfg.B * cfg.S
         unit = "query-tokens/s"
-        bound = "hbm" if args.config in ("decode", "ragged", "tiny") else "mfma"
-        workload = (f"{args.config} sparse_attn B={cfg.B} S={cfg.S} H={cfg.H} D={cfg.D} T={cfg.T} K={cfg.K}, "
-                    f"{nsets} rotating input sets")
+        bound = "hbm" if args.config in ("decode", "decode_fp8", "ragged", "tiny") else "mfma"
+        workload = (f"{args.config} sparse_attn{'_fp8 (584-byte MODEL1 rows)' if fp8 else ''} B={cfg.B} S={cfg.S} "
+                    f"H={cfg.H} D={cfg.D} T={cfg.T} K={cfg.K}, {nsets} rotating input sets")
         extra_cfg = {"B": cfg.B, "S": cfg.S, "H": cfg.H, "D": cfg.D, "T": cfg.T, "K": cfg.K,
                      "num_splits": sa.sparse_attn_num_splits(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)}
 
         def make_cpu(orc):
             x = sets[0]
-            qb, kvb = oracle_bits(x["q"]), oracle_bits(x["kv"])
+            qb = oracle_bits(x["q"])
             sk, ix = x["attn_sink"].cpu().numpy(), x["topk_idxs"].cpu().numpy()
             ntok = cfg.B * cfg.S
             toks = np.arange(ntok) if args.config != "prefill" else np.arange(0, ntok, 64)
+            if fp8:
+                kv8 = x["kv"].cpu().numpy()
+                return (lambda: orc.sparse_attn_fp8(qb, kv8, sk, ix, x["scale"], toks)), len(toks)
+            kvb = oracle_bits(x["kv"])
             return (lambda: orc.sparse_attn(qb, kvb, sk, ix, x["scale"], toks)), len(toks)
 
         sample_desc = ("all tokens of one step" if args.config != "prefill" else "every 64th token of one step")
@@ -331,7 +347,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bitmask": "int32", "candidate": "f32", "candidate_long": "f32"}.get(args.config, "bf16"),
+        "dtype": {"bitmask": "int32", "candidate": "f32", "candidate_long": "f32",
+                  "decode_fp8": "fp8-e4m3 rows, bf16 MFMA"}.get(args.config, "bf16"),
         "data": "synthetic",
         "config": {"workload": workload, **extra_cfg},
         "roofline": roof,

@@ -116,6 +116,25 @@ int sparse_attn_merge_fwd(const void* q, const void* kv, const float* attn_sink,
                           int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sparse_attn_fwd over FP8 rows (D = 512): the MODEL1 row of FlashMLA (DeepSeek V4
+ * source notes, ch. 5, section 5.7): 584 bytes per row of kv8 [B][T][584]:
+ *   bytes 0..447    e4m3 (OCP FP8 E4M3) values of dims 0..447,
+ *   bytes 448..575  bf16 (little-endian) dims 448..511 (the RoPE part, used as is),
+ *   bytes 576..582  one scale byte s per 64-dim tile of dims 0..447, byte 583 unused;
+ *   dim d < 448 is e4m3(byte d) * 2^(s[d / 64] - 127).
+ * The page prints the layout but not the scale byte's encoding; the unsigned
+ * power-of-two (UE8M0) reading above is this library's. Rows are dequantized to
+ * bf16 inside the kernel (exact for scale bytes in [15, 239], where every scaled
+ * e4m3 value is a normal bf16) and the call is otherwise sparse_attn_fwd with
+ * D = 512: same q, attn_sink, topk_idxs, out, scale, num_splits and workspace
+ * (size it with sparse_attn_workspace_bytes(B, S, H, 512, K, num_splits)).
+ * Requires kv8 8-byte aligned and T * 584 < 2^31.
+ */
+int sparse_attn_fp8_fwd(const void* q, const void* kv8, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                        int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int num_splits,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Bit-packed top-k mask.                                                    */
 /* Shape rule and row layout: prhub summary of vLLM PR #52217, key source    */

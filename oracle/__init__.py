@@ -18,6 +18,8 @@ Sources, per function:
   masked_attn_offset   prhub summary of vLLM PR #48770, key source (offset_dense_mask_mod:
                        chunked context, key index + key_start from the reserved word)
   candidate_mask       prhub summary of vLLM PR #56628 (the indexer's candidate-mask rule)
+  sparse_attn_fp8      as sparse_attn, over FP8 rows in the MODEL1 layout of "DeepSeek V4
+                       源码剖析" ch. 5, section 5.7 (448 e4m3 + 64 bf16 + 8 scale bytes)
 """
 from __future__ import annotations
 
@@ -65,6 +67,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_masked_attn.restype = ctypes.c_int
     lib.oracle_masked_attn_offset.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, ctypes.c_double, P, I]
     lib.oracle_masked_attn_offset.restype = ctypes.c_int
+    lib.oracle_sparse_attn_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, ctypes.c_double, P, I]
+    lib.oracle_sparse_attn_fp8.restype = ctypes.c_int
+    lib.oracle_fp8_dequant.argtypes = [P, P, I]
+    lib.oracle_fp8_dequant.restype = ctypes.c_int
     lib.oracle_candidate_mask.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I]
     lib.oracle_candidate_mask.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -121,6 +127,39 @@ class Oracle:
             B, S, H, D, T, K, float(scale), self._ptr(tokens), len(tokens))
         if rc != 0:
             raise ValueError("sparse_attn oracle rejected its arguments")
+        return out
+
+    def sparse_attn_fp8(self, q_bits, kv8, sink, idx, scale, tokens=None) -> np.ndarray:
+        """sparse_attn over FP8 rows: kv8 [B,T,584] uint8 (D = 512). Returns float64 [len(tokens), H, 512]."""
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        kv8 = np.ascontiguousarray(kv8, dtype=np.uint8)
+        sink = np.ascontiguousarray(sink, dtype=np.float32)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        B, S, H, D = q_bits.shape
+        Bk, T, R = kv8.shape
+        K = idx.shape[2]
+        if D != 512 or R != 584 or Bk != B or sink.shape != (H,) or idx.shape[:2] != (B, S):
+            raise ValueError("sparse_attn_fp8 oracle: inconsistent shapes")
+        if tokens is None:
+            tokens = np.arange(B * S, dtype=np.int64)
+        tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+        out = np.empty((len(tokens), H, D), dtype=np.float64)
+        rc = self.lib.oracle_sparse_attn_fp8(
+            self._ptr(q_bits), self._ptr(kv8), self._ptr(sink), self._ptr(idx), self._ptr(out),
+            B, S, H, T, K, float(scale), self._ptr(tokens), len(tokens))
+        if rc != 0:
+            raise ValueError("sparse_attn_fp8 oracle rejected its arguments")
+        return out
+
+    def fp8_dequant(self, kv8) -> np.ndarray:
+        """Dequantized rows: kv8 [..., 584] uint8 -> float64 [..., 512]."""
+        kv8 = np.ascontiguousarray(kv8, dtype=np.uint8)
+        if kv8.shape[-1] != 584:
+            raise ValueError("fp8_dequant oracle: rows are 584 bytes")
+        n = kv8.size // 584
+        out = np.empty(kv8.shape[:-1] + (512,), dtype=np.float64)
+        if self.lib.oracle_fp8_dequant(self._ptr(kv8), self._ptr(out), n) != 0:
+            raise ValueError("fp8_dequant oracle rejected its arguments")
         return out
 
     def topk_mask_shape(self, B, max_q, max_key, reserve_key_start_word=False) -> tuple[int, int, int]:

@@ -26,6 +26,8 @@
  *            prefill": key-source section (dense_mask_mod: word = kv >> 5,
  *            bit = kv & 31, LSB first; offset_dense_mask_mod reads key_start
  *            from the last word of query row 0 and adds it to the key index).
+ *            section 5.7 (FlashMLA's MODEL1 FP8 row: 448 e4m3 bytes, 64 bf16
+ *            RoPE dims, 8 scale bytes for 64-dim quantisation tiles).
  *  [PR56628] prhub summary of vLLM PR #56628 "ROCm DSA decode mask strides to
  *            each row's end": the candidate-mask rule (live columns
  *            [start, end), per-block keep flags relative to start, the edge
@@ -54,6 +56,43 @@ static double bf16_bits_to_double(uint16_t bits) {
   return (double)f;
 }
 
+/* OCP FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ * field 0 holds the subnormals m/8 * 2^-6; 0x7F and 0xFF are NaN; there is no infinity. */
+static double e4m3_to_double(uint8_t x) {
+  const int sgn = x >> 7, e = (x >> 3) & 15, m = x & 7;
+  double v;
+#if ORACLE_MUTANT == 19
+  v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 8); /* mutant: bias 8 */
+#else
+  if (e == 15 && m == 7) return NAN;
+  v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+#endif
+  return sgn ? -v : v;
+}
+
+/* Unsigned power-of-two scale byte (UE8M0): 2^(s - 127); 255 is NaN. */
+static double ue8m0_to_double(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* FP8 row layout (MODEL1 row of [DSV4-5] section 5.7, 584 bytes for D = 512): bytes 0..447
+ * e4m3 values of dims 0..447, bytes 448..575 the bf16 (little-endian) dims 448..511,
+ * bytes 576..582 one scale byte per 64-dim tile of the e4m3 part, byte 583 padding.
+ * Dim d < 448 is e4m3(byte d) * 2^(scale[d / 64] - 127). The scale byte encoding is not
+ * printed on the page; UE8M0 is this oracle's reading. */
+#define FP8_ROW_BYTES 584
+#define FP8_NOPE 448
+static double fp8_row_value(const uint8_t* row, int64_t d) {
+  if (d < FP8_NOPE) {
+#if ORACLE_MUTANT == 18
+    const int64_t tile = d / 64 + (d >= 64); /* mutant: tile index off by one past the first tile */
+#else
+    const int64_t tile = d / 64;
+#endif
+    return e4m3_to_double(row[d]) * ue8m0_to_double(row[FP8_NOPE + 128 + tile]);
+  }
+  const uint8_t* p = row + FP8_NOPE + 2 * (d - FP8_NOPE);
+  return bf16_bits_to_double((uint16_t)(p[0] | (p[1] << 8)));
+}
+
 /* ------------------------------------------------------------------------ */
 /* sparse_attn  ([DSV4-5] sections 5.1, 5.2, 5.4, 5.5)                       */
 /* ------------------------------------------------------------------------ */
@@ -72,11 +111,18 @@ static double bf16_bits_to_double(uint16_t bits) {
  * o = 0; no valid slot and sink -inf -> o = 0 (empty softmax taken as zero).
  * Returns 0, or -1 on a bad argument.
  */
-int oracle_sparse_attn(const uint16_t* q, const uint16_t* kv, const float* sink, const int32_t* idx, double* out,
-                       int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, double scale,
-                       const int64_t* tokens, int64_t ntok) {
+/* kv row element: bf16 rows [B][T][D] (fp8 == 0) or FP8 rows [B][T][584] (fp8 != 0, D = 512) */
+static double kv_value(const void* kv, int fp8, int64_t b, int64_t T, int64_t D, int64_t j, int64_t d) {
+  if (fp8) return fp8_row_value((const uint8_t*)kv + (b * T + j) * FP8_ROW_BYTES, d);
+  return bf16_bits_to_double(((const uint16_t*)kv)[(b * T + j) * D + d]);
+}
+
+static int sparse_attn_impl(const uint16_t* q, const void* kv, int fp8, const float* sink, const int32_t* idx,
+                            double* out, int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K,
+                            double scale, const int64_t* tokens, int64_t ntok) {
   if (!q || !kv || !sink || !idx || !out || !tokens) return -1;
   if (B < 0 || S < 0 || H < 0 || D < 0 || T < 0 || K < 0 || ntok < 0) return -1;
+  if (fp8 && D != 512) return -1;
   for (int64_t i = 0; i < ntok; i++)
     if (tokens[i] < 0 || tokens[i] >= B * S) return -1;
 
@@ -104,9 +150,8 @@ int oracle_sparse_attn(const uint16_t* q, const uint16_t* kv, const float* sink,
         if (j == -1) j = T - 1; /* mutant: -1 read as the last row (python negative index) */
 #endif
         if (j < 0 || j >= T) continue;
-        const uint16_t* row = kv + (b * T + j) * D;
         double dot = 0.0;
-        for (int64_t d = 0; d < D; d++) dot += bf16_bits_to_double(qv[d]) * bf16_bits_to_double(row[d]);
+        for (int64_t d = 0; d < D; d++) dot += bf16_bits_to_double(qv[d]) * kv_value(kv, fp8, b, T, D, j, d);
 #if ORACLE_MUTANT == 3
         x[k] = dot; /* mutant: scale dropped */
 #else
@@ -140,13 +185,36 @@ int oracle_sparse_attn(const uint16_t* q, const uint16_t* kv, const float* sink,
 #endif
         const double p = exp(x[k] - m);
         l += p;
-        const uint16_t* row = kv + (b * T + j) * D;
-        for (int64_t d = 0; d < D; d++) o[d] += p * bf16_bits_to_double(row[d]);
+        for (int64_t d = 0; d < D; d++) o[d] += p * kv_value(kv, fp8, b, T, D, j, d);
       }
       for (int64_t d = 0; d < D; d++) o[d] /= l;
     }
     free(x);
   }
+  return 0;
+}
+
+int oracle_sparse_attn(const uint16_t* q, const uint16_t* kv, const float* sink, const int32_t* idx, double* out,
+                       int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, double scale,
+                       const int64_t* tokens, int64_t ntok) {
+  return sparse_attn_impl(q, kv, 0, sink, idx, out, B, S, H, D, T, K, scale, tokens, ntok);
+}
+
+/*
+ * The same computation over FP8 rows: kv8 [B][T][584] bytes in the row layout above
+ * (D = 512), each row dequantized exactly before use.
+ */
+int oracle_sparse_attn_fp8(const uint16_t* q, const uint8_t* kv8, const float* sink, const int32_t* idx, double* out,
+                           int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, double scale,
+                           const int64_t* tokens, int64_t ntok) {
+  return sparse_attn_impl(q, kv8, 1, sink, idx, out, B, S, H, 512, T, K, scale, tokens, ntok);
+}
+
+/* Dequantized FP8 rows (for checks): out [n][512] double for rows kv8 [n][584]. */
+int oracle_fp8_dequant(const uint8_t* kv8, double* out, int64_t n) {
+  if (!kv8 || !out || n < 0) return -1;
+  for (int64_t j = 0; j < n; j++)
+    for (int64_t d = 0; d < 512; d++) out[j * 512 + d] = fp8_row_value(kv8 + j * FP8_ROW_BYTES, d);
   return 0;
 }
 

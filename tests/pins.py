@@ -542,6 +542,67 @@ def check_candmask_row_repeat_and_page_ends(o):
         assert np.array_equal(_kept(got2[r]), np.arange(half[r // 2])), r
 
 
+# --------------------------------------------------------------------------- FP8 row pins
+def _fp8_rows(seed, n, scale_lo=118, scale_hi=136):
+    """Random FP8 rows (584 bytes: 448 e4m3, 64 bf16, 7 scales + pad) without NaN bytes."""
+    g = np.random.default_rng(seed)
+    rows = g.integers(0, 256, size=(n, 584), dtype=np.uint8)
+    nan = (rows[:, :448] & 0x7F) == 0x7F
+    rows[:, :448][nan] ^= 0x01
+    rope = torch.randn(n, 64, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    rows[:, 448:576] = rope.view(torch.int16).numpy().view(np.uint8).reshape(n, 128)
+    rows[:, 576:583] = g.integers(scale_lo, scale_hi + 1, size=(n, 7), dtype=np.uint8)
+    rows[:, 583] = 0
+    return rows
+
+
+def _fp8_decode_torch(rows):
+    """Dequantized rows through torch's float8_e4m3fn and bfloat16 decoders (float64)."""
+    t = torch.from_numpy(rows)
+    fp8 = t[:, :448].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+    sc = torch.pow(2.0, t[:, 576:583].to(torch.float64) - 127.0).repeat_interleave(64, dim=1)
+    rope = t[:, 448:576].contiguous().view(torch.bfloat16).to(torch.float64)
+    return torch.cat([fp8 * sc, rope], dim=1).numpy()
+
+
+def check_fp8_decode_matches_torch(o):
+    """Every non-NaN e4m3 byte, at several scale bytes, and the bf16 RoPE dims decode as torch's
+    float8_e4m3fn / bfloat16 do, times 2^(scale - 127) per 64-dim tile (MODEL1 row layout)."""
+    rows = _fp8_rows(41, 6, scale_lo=100, scale_hi=160)
+    allb = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
+    rows[0, :len(allb)] = allb
+    rows[1, :len(allb)] = allb[::-1]
+    assert np.array_equal(o.fp8_dequant(rows), _fp8_decode_torch(rows))
+    one = np.zeros((1, 584), dtype=np.uint8)
+    one[0, [0, 1, 2, 64]] = [0x38, 0x7E, 0x01, 0x40]   # 1, 448, 2^-9 (subnormal), 2
+    one[0, 576:583] = [127, 128, 127, 127, 127, 127, 127]
+    d = o.fp8_dequant(one)[0]
+    assert d[0] == 1.0 and d[1] == 448.0 and d[2] == 2.0 ** -9 and d[64] == 4.0
+
+
+def check_fp8_attention_equals_bf16_rows(o):
+    """Sparse attention over FP8 rows equals it over the same rows written as bf16 (exact: the
+    scaled e4m3 values fit bf16), and one valid slot with sink -inf returns that row."""
+    g = torch.Generator().manual_seed(42)
+    B, S, H, T, K = 2, 2, 3, 30, 10
+    rows = _fp8_rows(43, B * T)
+    dec = _fp8_decode_torch(rows)
+    kv16 = torch.from_numpy(dec).to(torch.bfloat16)
+    assert np.array_equal(kv16.to(torch.float64).numpy(), dec)
+    q = torch.randn(B, S, H, 512, generator=g).to(torch.bfloat16)
+    idx = torch.stack([torch.randperm(T, generator=g)[:K] for _ in range(B * S)]).view(B, S, K).to(torch.int32)
+    idx[0, 1, 2] = -1
+    sink = torch.randn(H, generator=g)
+    scale = 512 ** -0.5
+    a = o.sparse_attn_fp8(_bits(q), rows.reshape(B, T, 584), sink.numpy(), idx.numpy(), scale)
+    b = o.sparse_attn(_bits(q), _bits(kv16.view(B, T, 512)), sink.numpy(), idx.numpy(), scale)
+    assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(b).max())
+    one = np.full((B, S, K), -1, dtype=np.int32)
+    one[1, 0, 4] = 7
+    c = o.sparse_attn_fp8(_bits(q), rows.reshape(B, T, 584), np.full(H, -np.inf, dtype=np.float32), one, scale)
+    assert np.array_equal(c[2], np.broadcast_to(dec[T + 7], (H, 512)))
+
+
 SPARSE_PINS = [check_loop_semantics, check_all_invalid_zero, check_order_invariance, check_dense_equivalence,
                check_sink_extra_key, check_exact_mean, check_sink_halves, check_single_row, check_inf_nan_sink,
                check_huge_sink, check_duplicates_count, check_scale_closed_form, check_out_of_range_is_empty]
@@ -550,4 +611,5 @@ MASK_PINS = [check_mask_worked_example, check_mask_brute_force, check_mask_singl
 MASKED_PINS = [check_masked_dense, check_masked_random, check_two_forms_agree, check_offset_chunk_is_sdpa,
                check_offset_zero_start_is_plain, check_offset_stops_at_reserved_word]
 CANDIDATE_PINS = [check_candmask_closed_forms, check_candmask_single_block, check_candmask_row_repeat_and_page_ends]
-ALL_PINS = SPARSE_PINS + MASK_PINS + MASKED_PINS + CANDIDATE_PINS
+FP8_PINS = [check_fp8_decode_matches_torch, check_fp8_attention_equals_bf16_rows]
+ALL_PINS = SPARSE_PINS + MASK_PINS + MASKED_PINS + CANDIDATE_PINS + FP8_PINS

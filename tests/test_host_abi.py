@@ -144,6 +144,18 @@ def test_candidate_grid_depends_on_shapes_only():
     assert sa.candidate_mask_grid(0, 100) == 0
 
 
+def _fp8(q=FAKE, kv=FAKE, sink=FAKE, idx=FAKE, out=FAKE, B=1, S=1, H=8, T=16, K=8, ws=None, wsb=0):
+    return _lib().sparse_attn_fp8_fwd(q, kv, sink, idx, out, B, S, H, T, K, 0.1, 0, ws, wsb, None)
+
+
+def test_sparse_fp8_rejects_before_any_hip_call():
+    assert _fp8(T=(1 << 31) // 584 + 1) == 2   # rows past 2^31 bytes
+    assert _fp8(kv=ctypes.c_void_p((1 << 20) + 4)) == 3  # rows need 8-byte alignment
+    assert _fp8(H=129) == 4
+    assert _fp8(idx=None) == 1
+    assert _fp8(B=0) == 0
+
+
 def test_status_strings():
     for s in range(7):
         assert _lib().sa_status_string(s)

@@ -28,6 +28,8 @@ MUTANTS = {
     15: "chunked form reads the reserved word as mask bits",
     16: "candidate blocks counted from column 0 instead of the start",
     17: "candidate edge flag ignored",
+    18: "FP8 scale tile index off by one",
+    19: "e4m3 exponent bias 8",
 }
 
 

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     masked_attn_offset,
     new_workspace,
     sparse_attn,
+    sparse_attn_fp8,
     sparse_attn_merge,
     sparse_attn_split,
     sparse_attn_num_splits,

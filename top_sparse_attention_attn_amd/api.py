@@ -22,7 +22,7 @@ SA_STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_ALIGN",
              5: "SA_ERR_WORKSPACE", 6: "SA_ERR_HIP"}
 
 EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_fwd",
-            "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "topk_bitmask_shape", "topk_bitmask_build",
+            "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "sparse_attn_fp8_fwd", "topk_bitmask_shape", "topk_bitmask_build",
             "masked_attn_fwd", "masked_attn_offset_fwd", "candidate_mask_apply", "candidate_mask_grid"]
 
 
@@ -55,6 +55,8 @@ def _load():
         for name in ("sparse_attn_fwd", "sparse_attn_split_fwd", "sparse_attn_merge_fwd"):
             getattr(lib, name).argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
             getattr(lib, name).restype = I
+        lib.sparse_attn_fp8_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
+        lib.sparse_attn_fp8_fwd.restype = I
         lib.topk_bitmask_shape.argtypes = [I64, I64, I64, I, P]
         lib.topk_bitmask_shape.restype = I
         lib.topk_bitmask_build.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P]
@@ -172,10 +174,20 @@ def sparse_attn_merge(q, kv, attn_sink, topk_idxs, scale, out, num_splits: int =
     return _sparse_call("sparse_attn_merge_fwd", q, kv, attn_sink, topk_idxs, scale, out, num_splits, workspace)
 
 
+def sparse_attn_fp8(q: torch.Tensor, kv8: torch.Tensor, attn_sink: torch.Tensor, topk_idxs: torch.Tensor,
+                    scale: float, out: torch.Tensor | None = None, num_splits: int = 0,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """sparse_attn over FP8 rows: kv8 [B,T,584] uint8 in the MODEL1 row layout (448 e4m3 bytes,
+    64 bf16 RoPE dims, 7 scale bytes + 1 pad; dim d < 448 = e4m3 * 2^(scale[d // 64] - 127)).
+    q [B,S,H,512] bf16; otherwise as sparse_attn."""
+    return _sparse_call("sparse_attn_fp8_fwd", q, kv8, attn_sink, topk_idxs, scale, out, num_splits, workspace)
+
+
 def _sparse_call(entry, q, kv, attn_sink, topk_idxs, scale, out, num_splits, workspace):
     dev = q.device
+    fp8 = entry == "sparse_attn_fp8_fwd"
     _check(q, "q", torch.bfloat16)
-    _check(kv, "kv", torch.bfloat16, dev)
+    _check(kv, "kv", torch.uint8 if fp8 else torch.bfloat16, dev)
     _check(attn_sink, "attn_sink", torch.float32, dev)
     _check(topk_idxs, "topk_idxs", torch.int32, dev)
     if q.dim() != 4 or kv.dim() != 3 or topk_idxs.dim() != 3 or attn_sink.dim() != 1:
@@ -183,7 +195,8 @@ def _sparse_call(entry, q, kv, attn_sink, topk_idxs, scale, out, num_splits, wor
     B, S, H, D = q.shape
     T = kv.shape[1]
     K = topk_idxs.shape[2]
-    if kv.shape[0] != B or kv.shape[2] != D or attn_sink.shape[0] != H or tuple(topk_idxs.shape[:2]) != (B, S):
+    if kv.shape[0] != B or kv.shape[2] != (584 if fp8 else D) or attn_sink.shape[0] != H or \
+            tuple(topk_idxs.shape[:2]) != (B, S) or (fp8 and D != 512):
         raise ValueError("inconsistent shapes")
     if out is None:
         out = torch.empty_like(q)
@@ -193,8 +206,12 @@ def _sparse_call(entry, q, kv, attn_sink, topk_idxs, scale, out, num_splits, wor
             raise ValueError("out must have q's shape")
     need = sparse_attn_workspace_bytes(B, S, H, D, K, num_splits)
     ws, ws_bytes = _workspace(dev, need, workspace)
-    _call(entry, _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, S, H, D, T, K,
-          float(scale), int(num_splits), _ptr(ws), ws_bytes, _stream_ptr(dev))
+    if fp8:
+        _call(entry, _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, S, H, T, K,
+              float(scale), int(num_splits), _ptr(ws), ws_bytes, _stream_ptr(dev))
+    else:
+        _call(entry, _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, S, H, D, T, K,
+              float(scale), int(num_splits), _ptr(ws), ws_bytes, _stream_ptr(dev))
     return out
 
 

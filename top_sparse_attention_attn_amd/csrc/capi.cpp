@@ -9,7 +9,7 @@
 extern "C" {
 int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
                               int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
-                              int nsplit, void* ws, int phases, void* stream);
+                              int nsplit, void* ws, int phases, int fp8, void* stream);
 int sa_internal_head_blocks(int64_t H);
 size_t sa_internal_sparse_ws_bytes(int64_t ntok, int64_t H, int64_t D, int nsplit);
 int sa_internal_launch_bitmask(const int32_t* idx, const int32_t* q_lens, const int32_t* key_starts, uint32_t* mask,
@@ -58,14 +58,17 @@ size_t sparse_ws_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int nsplit) {
 
 static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
                            int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
-                           int num_splits, void* workspace, size_t workspace_bytes, void* stream, int phases) {
+                           int num_splits, void* workspace, size_t workspace_bytes, void* stream, int phases,
+                           int fp8 = 0) {
   if (!sparse_sizes_ok(B, S, H, D, K) || T < 0 || num_splits < 0 || num_splits > 64) return SA_ERR_SHAPE;
   if (B * S == 0 || H == 0) return SA_OK;
   if (D != 64 && D != 512) return SA_ERR_UNSUPPORTED;
+  if (fp8 && (D != 512 || T * 584 > ((int64_t)1 << 31) - 1)) return fp8 && D != 512 ? SA_ERR_UNSUPPORTED : SA_ERR_SHAPE;
+  if (fp8 && kv && ((uintptr_t)kv & 7u)) return SA_ERR_ALIGN;
   if (H > 128) return SA_ERR_UNSUPPORTED;
   if (B * S > (int64_t)1 << 30 || T > (int64_t)1 << 31 || K > (int64_t)1 << 30) return SA_ERR_SHAPE;
   if (!q || !attn_sink || !out || (K > 0 && !topk_idxs) || (T > 0 && K > 0 && !kv)) return SA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || (kv && !aligned16(kv))) return SA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(out) || (!fp8 && kv && !aligned16(kv))) return SA_ERR_ALIGN;
   if (((uintptr_t)attn_sink & 3u) || (topk_idxs && ((uintptr_t)topk_idxs & 3u))) return SA_ERR_ALIGN;
   const int nsplit = choose_splits(B, S, K, num_splits);
   const size_t need = sparse_ws_bytes(B, S, H, D, nsplit);
@@ -74,7 +77,7 @@ static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink
     if ((uintptr_t)workspace & 255u) return SA_ERR_ALIGN;
   }
   const int rc = sa_internal_launch_sparse(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, nsplit,
-                                           need > 0 ? workspace : nullptr, phases, stream);
+                                           need > 0 ? workspace : nullptr, phases, fp8, stream);
   return rc == 0 ? SA_OK : SA_ERR_HIP;
 }
 
@@ -141,6 +144,13 @@ int sparse_attn_merge_fwd(const void* q, const void* kv, const float* attn_sink,
                           void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_attn_run(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, num_splits, workspace,
                          workspace_bytes, stream, 2);
+}
+
+int sparse_attn_fp8_fwd(const void* q, const void* kv8, const float* attn_sink, const int32_t* topk_idxs, void* out,
+                        int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int num_splits,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attn_run(q, kv8, attn_sink, topk_idxs, out, B, S, H, 512, T, K, scale, num_splits, workspace,
+                         workspace_bytes, stream, 3, 1);
 }
 
 int topk_bitmask_shape(int64_t B, int64_t max_q_len, int64_t max_key_len, int reserve_key_start_word,

@@ -26,6 +26,11 @@
 //  * Online softmax in base 2 with a lazily moved reference maximum: the output is
 //    rescaled only when a head's maximum grows by more than 2^8 (rare after the first
 //    tile); weights stay <= 2^8, so nothing overflows.
+//  * FP8 rows (the MODEL1 row of section 5.7: 448 e4m3 bytes, 64 bf16 RoPE dims, one scale
+//    byte per 64-dim tile, 584 bytes for D = 512): the value waves copy each row's bytes into
+//    its ring slot with buffer loads that write LDS, and one tile before the tile is used
+//    they expand it in place to the bf16 row (v_cvt_scalef32_pk_bf16_fp8, scale 2^(s-127)),
+//    so the scores and P V run unchanged on bf16 rows while HBM moves 584 bytes per row.
 #include <stddef.h>
 
 #include "common.h"
@@ -39,6 +44,8 @@ constexpr int kMaxSplits = 16;
 constexpr int kThreads = 768;   // 4 score waves + 8 value waves
 constexpr int kValueWaves = 8;
 constexpr int kPStride = kTile + 8;  // bf16 elements per P row in LDS (80 bytes)
+constexpr int kF8Row = 584;         // FP8 row: 448 e4m3 + 128 bytes of bf16 RoPE + 8 scale bytes
+constexpr int kF8Nope = 448;
 
 template <int D>
 struct Geo {
@@ -119,8 +126,8 @@ __device__ __forceinline__ void pv_step(Smem<D, HB>& sm, f32x4 (&oacc)[HB][NB > 
   }
 }
 
-template <int D, int HB, bool SCORE>
-__device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
+template <int D, int HB, bool SCORE, bool F8>
+__device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restrict__ q, const void* __restrict__ kv,
                                           const float* __restrict__ sink, const int* __restrict__ idx,
                                           __bf16* __restrict__ out, __bf16* __restrict__ ws_o,
                                           float* __restrict__ ws_lse, int S, int H, int T, int K, int nsplit,
@@ -148,7 +155,10 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   const int t0 = (int)(((long)split * ntiles_all) / nsplit);
   const int ntl = (int)(((long)(split + 1) * ntiles_all) / nsplit) - t0;
   const int* __restrict__ idx_tok = idx + (size_t)tok * K;
-  const __bf16* __restrict__ kv_b = kv + (size_t)b * T * D;
+  const __bf16* __restrict__ kv_b = (const __bf16*)kv + (size_t)(F8 ? 0 : b) * T * D;
+  static_assert(!F8 || D == 512, "FP8 rows hold D = 512");
+  u32x4 kv8rs = {};  // FP8: the batch's rows as a buffer resource
+  if constexpr (F8) kv8rs = buffer_rsrc((const uint8_t*)kv + (size_t)b * T * kF8Row, (uint32_t)T * kF8Row);
 
   // ---- score waves: queries of head blocks sw and sw+4 (B operand of S^T = K Q^T)
   constexpr int QB = SCORE ? (HB > 4 ? 2 : 1) : 1;
@@ -200,7 +210,19 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     for (int r = 0; r < 4; r++) {
       const int row = rows[r];
       unsigned char* dst = &sm.kv[bi][(sw * 4 + r) * G::kRowStride];
-      if (row >= 0 && row < T) {
+      if constexpr (F8) {
+        // the row's first 576 bytes by lanes 0-35 (16 bytes each), its 8 scale bytes by lanes
+        // 0-1 (4 bytes each); the other lanes are inactive, so nothing else in the slot is
+        // written. An invalid row is zero-filled when the tile is expanded.
+        if (row >= 0 && row < T) {
+          vbits |= 1u << r;
+          n += 2;
+          const uint32_t base = (uint32_t)row * kF8Row;
+          const uint32_t ldst = lds_addr(dst);
+          if (lane < 36) dma_lds16(kv8rs, base + 16u * lane, ldst);
+          if (lane < 2) dma_lds4(kv8rs, base + 576u + 4u * lane, ldst + 576u);
+        }
+      } else if (row >= 0 && row < T) {
         vbits |= 1u << r;
         n++;
         if (lane < G::kLanesPerRow)
@@ -214,6 +236,56 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     return n;
   };
 
+  // FP8: expand this wave's 4 rows of tile tt in place from the copied bytes to bf16 rows
+  // (lanes 0-55: 8 e4m3 values of dims 8l .. 8l+7 with their tile's scale; lanes 56-63: 8 RoPE
+  // dims), invalid rows to zeros. All reads land before any write: the bf16 row overlaps the
+  // bytes it is made from. Called once the tile's copies have landed (this wave's own rows).
+  auto expand = [&](int tt) {
+    const int bi = tt % kBufs;
+    const unsigned vbits = __builtin_amdgcn_readfirstlane((unsigned)sm.vmb[bi][sw]);
+    uint2 f8[4];
+    uint4 rp[4];
+    unsigned sb[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const unsigned char* slot = &sm.kv[bi][(sw * 4 + r) * G::kRowStride];
+      f8[r] = make_uint2(0u, 0u);
+      rp[r] = make_uint4(0u, 0u, 0u, 0u);
+      sb[r] = 0u;
+      if (vbits & (1u << r)) {
+        if (lane < 56) {
+          f8[r] = *(const uint2*)(slot + 8 * lane);
+          sb[r] = slot[576 + (lane >> 3)];
+        } else {
+          rp[r] = *(const uint4*)(slot + kF8Nope + 16 * (lane - 56));
+        }
+      }
+    }
+    wait_lgkm0();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      unsigned char* slot = &sm.kv[bi][(sw * 4 + r) * G::kRowStride];
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (vbits & (1u << r)) {
+        if (lane < 56) {
+          // 2^(s-127) as an fp32 bit pattern (s = 0: the subnormal 2^-127; s = 255: NaN)
+          const unsigned bits = sb[r] == 0u ? 0x00400000u : (sb[r] == 255u ? 0x7fc00000u : sb[r] << 23);
+          const float sc = __uint_as_float(bits);
+          const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8[r].x, sc, false);
+          const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8[r].x, sc, true);
+          const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8[r].y, sc, false);
+          const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8[r].y, sc, true);
+          const bf16x8 v = bf16x8{a[0], a[1], c[0], c[1], d[0], d[1], e[0], e[1]};
+          w = *(const uint4*)&v;
+        } else {
+          w = rp[r];
+        }
+      }
+      *(uint4*)(slot + (lane < 56 ? 16 * lane : 2 * kF8Nope + 16 * (lane - 56))) = w;
+    }
+  };
+
   int rows_next[4];
   int dma_last = 0;  // DMA count of the most recently issued tile
   // Value waves start the gather of tiles 0 and 1 at once: it overlaps the query loads of the
@@ -224,6 +296,12 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
       load_rows(tt, rows);
       dma_last = issue(tt, rows);
     }
+    if constexpr (F8) {
+      if (0 < ntl) {
+        wait_vm_lgkm0_dyn(1 < ntl ? dma_last : 0);  // tile 0's copies have landed
+        expand(0);
+      }
+    }
     if (2 < ntl) load_rows(2, rows_next);
   } else {
     // Score waves win MFMA issue arbitration over the value waves of their SIMD, so the
@@ -233,12 +311,13 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 
   for (int tt = 0; tt <= ntl; tt++) {
     // Tile tt's rows have landed once only the younger tile's DMAs may still be pending.
-    if constexpr (SCORE) wait_lgkm0();
+    if constexpr (SCORE || F8) wait_lgkm0();  // FP8: the tile was expanded (and waited for) before
     else wait_vm_lgkm0_dyn(tt + 1 < ntl ? dma_last : 0);
     wg_barrier();  // tile tt and P(tt-1) visible; everyone is done with tile tt-2 and P(tt-2)
     // ---- prefetch tile tt+2 into the buffer freed by tile tt-2
+    int dma_new = 0;  // copies issued in this iteration (tile tt+2)
     if constexpr (!SCORE) {
-      if (tt + 2 < ntl) dma_last = issue(tt + 2, rows_next);
+      if (tt + 2 < ntl) dma_last = dma_new = issue(tt + 2, rows_next);
     }
     // ---- scores of tile tt (score waves)
     f32x4 sacc[QB][2];
@@ -363,6 +442,14 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         const int tp = tt - 1;
         if (tile_mask(sm, tp % kBufs) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, lane, g, l16);
       }
+      if constexpr (F8) {
+        // expand tile tt+1 for the next barrier: its copies (issued one tile ago) have landed
+        // once at most this iteration's copies are outstanding
+        if (tt + 1 < ntl) {
+          wait_vm_lgkm0_dyn(dma_new);
+          expand(tt + 1);
+        }
+      }
       // Index loads of tile tt+3 go out after PV: scalar loads share the LDS wait counter, so
       // issued earlier they would hold up every LDS wait of PV. Their latency overlaps this
       // wave's wait at the next barrier.
@@ -458,16 +545,16 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   if (tid < HP) ws_lse[(size_t)pair * HP + tid] = sm.lsef[tid];
 }
 
-template <int D, int HB>
+template <int D, int HB, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ kv, const float* __restrict__ sink,
+    const __bf16* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ sink,
     const int* __restrict__ idx, __bf16* __restrict__ out, __bf16* __restrict__ ws_o, float* __restrict__ ws_lse,
     int S, int H, int T, int K, int nsplit, int nxcc, float scale_log2) {
   __shared__ __attribute__((aligned(16))) Smem<D, HB> sm;
   if (threadIdx.x < 256)  // waves 0-3
-    run_split<D, HB, true>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, scale_log2);
+    run_split<D, HB, true, F8>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, scale_log2);
   else
-    run_split<D, HB, false>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, scale_log2);
+    run_split<D, HB, false, F8>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, scale_log2);
 }
 
 // Merge the split partials of one (token, 16-head block) and add the sink once:
@@ -610,7 +697,7 @@ static int device_xccs() {
   return cache[dev];
 }
 
-template <int D, int HB>
+template <int D, int HB, bool F8>
 static hipError_t launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
                                 int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int nsplit,
                                 void* ws, int phases, hipStream_t stream) {
@@ -621,8 +708,8 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
   float* ws_lse = nsplit > 1 ? (float*)((char*)ws + L.lse) : nullptr;
   const int nxcc = device_xccs();
   if (phases & 1) {
-    hipLaunchKernelGGL((sparse_attn_kernel<D, HB>), dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q,
-                       (const __bf16*)kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H, (int)T, (int)K, nsplit,
+    hipLaunchKernelGGL((sparse_attn_kernel<D, HB, F8>), dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q,
+                       kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H, (int)T, (int)K, nsplit,
                        nxcc, scale * kLog2e);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -642,20 +729,27 @@ extern "C" int sa_internal_head_blocks(int64_t H) {
 }
 
 // phases: bit 0 = the main kernel, bit 1 = the merge of the split partials (if any)
+// fp8: kv holds FP8 rows of 584 bytes (D = 512)
 extern "C" int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx,
                                          void* out, int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K,
-                                         float scale, int nsplit, void* ws, int phases, void* stream) {
+                                         float scale, int nsplit, void* ws, int phases, int fp8, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int hb = sa_internal_head_blocks(H);
   hipError_t e;
 #define SA_CASE(DD, HBB) \
-  e = sa::launch_sparse<DD, HBB>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, phases, st)
-  if (D == 512) {
+  e = sa::launch_sparse<DD, HBB, false>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, phases, st)
+#define SA_CASE8(HBB) \
+  e = sa::launch_sparse<512, HBB, true>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, phases, st)
+  if (fp8) {
+    if (D != 512) return 2;
+    if (hb == 1) SA_CASE8(1); else if (hb == 2) SA_CASE8(2); else if (hb == 4) SA_CASE8(4); else SA_CASE8(8);
+  } else if (D == 512) {
     if (hb == 1) SA_CASE(512, 1); else if (hb == 2) SA_CASE(512, 2); else if (hb == 4) SA_CASE(512, 4); else SA_CASE(512, 8);
   } else {
     if (hb == 1) SA_CASE(64, 1); else if (hb == 2) SA_CASE(64, 2); else if (hb == 4) SA_CASE(64, 4); else SA_CASE(64, 8);
   }
 #undef SA_CASE
+#undef SA_CASE8
   return e == hipSuccess ? 0 : 1;
 }
 

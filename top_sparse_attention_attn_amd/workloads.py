@@ -210,3 +210,24 @@ def candidate_inputs(cfg: CandidateConfig | str, seed: int, device="cpu", keep_p
     logits = torch.randn((cfg.rows, cfg.width), generator=_dev_gen(seed * 3 + 1, device), device=device)
     return {"logits": logits, "ends": ends.to(device), "flags": flags.to(device), "block_size": cfg.block_size,
             "config": cfg, "seed": seed}
+
+
+def fp8_kv_rows(B: int, T: int, seed: int, device="cpu") -> torch.Tensor:
+    """[B, T, 584] uint8 FP8 rows in the MODEL1 layout: N(0,1) values of dims 0..447 quantised
+    per 64-dim tile with a power-of-two scale byte (the smallest 2^e with amax / 2^e <= 448,
+    stored as e + 127) through torch's float8_e4m3fn, N(0,1) bf16 dims 448..511, a zero pad byte."""
+    g = _dev_gen(seed, device)
+    n = B * T
+    rows = torch.empty((n, 584), dtype=torch.uint8, device=device)
+    step = 1 << 18
+    for a in range(0, n, step):
+        m = min(step, n - a)
+        x = torch.randn((m, 7, 64), generator=g, device=device)
+        e = torch.ceil(torch.log2(x.abs().amax(dim=2).clamp_min(1e-30) / 448.0)).clamp(-120, 120)
+        qv = (x / torch.pow(2.0, e).unsqueeze(2)).to(torch.float8_e4m3fn)
+        rows[a:a + m, :448] = qv.view(torch.uint8).reshape(m, 448)
+        rope = torch.randn((m, 64), generator=g, device=device).to(torch.bfloat16)
+        rows[a:a + m, 448:576] = rope.view(torch.uint8).reshape(m, 128)
+        rows[a:a + m, 576:583] = (e + 127).to(torch.uint8)
+        rows[a:a + m, 583] = 0
+    return rows.view(B, T, 584)
