@@ -9,7 +9,8 @@ H=128, D=512, K=1152 (128 window + 1024 selected slots, ~5% empty) over a
 kv cache of 128 + 8192 rows. Steps cycle through 8 independent input sets
 (~4.4 GB in total), so no step finds its rows left in the 256 MB Infinity Cache
 by an earlier step. The timed region is bracketed by device synchronisations
-and measured with HIP events recorded on the stream the kernels run on.
+and measured with HIP events recorded on the stream the kernels run on; the dominant
+kernel is then timed alone with an event pair around each launch.
 
 Prints one JSON line: the metric, throughput, milliseconds per step, the
 roofline fraction of the whole call (algorithmic bytes counted from the actual
@@ -303,14 +304,21 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
-    # The dominant kernel alone, timed the same way on the same stream.
+    # The dominant kernel alone, on the same stream: one event pair around every launch, so the
+    # average is each launch's own duration (what a kernel trace reports), without the overlap
+    # of one launch's tail with the next launch's start that back-to-back timing includes.
     torch.cuda.synchronize()
-    e0.record(stream)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # A short spin on the stream first lets the host queue every launch before the GPU reaches
+    # them, so no pair also times the host's launch overhead (it matters for kernels shorter
+    # than a Python-side launch).
+    torch.cuda._sleep(int(2.4e6 * max(1.0, 0.02 * args.steps)))
     for i in range(args.steps):
+        pairs[i][0].record(stream)
         kernel_step(i)
-    e1.record(stream)
+        pairs[i][1].record(stream)
     torch.cuda.synchronize()
-    kms = e0.elapsed_time(e1) / args.steps
+    kms = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
 
     nbytes = sum(w[0] for w in work) / len(work)
     flops = sum(w[1] for w in work) / len(work)

@@ -41,7 +41,7 @@ def _one(pattern: str) -> str:
 
 
 def _ours(name: str) -> bool:
-    return "sparse_attn" in name or "topk_bitmask" in name or "masked_attn" in name
+    return any(k in name for k in ("sparse_attn", "topk_bitmask", "masked_attn", "candidate_mask"))
 
 
 def kernel_stats(trace_dir: str):
