@@ -38,7 +38,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--config", default="decode", choices=["decode", "decode_fp8", "prefill", "ragged", "masked", "bitmask", "tiny",
                                                         "candidate", "candidate_long"])
     p.add_argument("--sets", type=int, default=NSETS)

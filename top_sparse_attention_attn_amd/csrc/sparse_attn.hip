@@ -438,17 +438,18 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     }
     // ---- P V for the previous tile (value waves)
     if constexpr (!SCORE) {
-      if (tt >= 1 && pv_active) {
-        const int tp = tt - 1;
-        if (tile_mask(sm, tp % kBufs) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, lane, g, l16);
-      }
       if constexpr (F8) {
-        // expand tile tt+1 for the next barrier: its copies (issued one tile ago) have landed
-        // once at most this iteration's copies are outstanding
+        // expand tile tt+1 for the next barrier, before P V so that its LDS round trips overlap
+        // the score waves' work: its copies (issued one tile ago) have landed once at most this
+        // iteration's copies are outstanding
         if (tt + 1 < ntl) {
           wait_vm_lgkm0_dyn(dma_new);
           expand(tt + 1);
         }
+      }
+      if (tt >= 1 && pv_active) {
+        const int tp = tt - 1;
+        if (tile_mask(sm, tp % kBufs) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, lane, g, l16);
       }
       // Index loads of tile tt+3 go out after PV: scalar loads share the LDS wait counter, so
       // issued earlier they would hold up every LDS wait of PV. Their latency overlaps this
