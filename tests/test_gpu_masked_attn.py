@@ -194,3 +194,44 @@ def test_offset_masked_config_sampled(oracle_impl):
     ref = _offset_ref(oracle_impl, inp, k, v, mask, rows)
     got = to64(out.reshape(cfg.B * cfg.Q, cfg.H, cfg.Dv)[torch.as_tensor(rows, device=DEV)])
     assert_close(got, ref, "offset masked config")
+
+
+# --------------------------------------------------------------------------- bounds and graph replay
+@pytest.mark.parametrize("offset", [False, True])
+def test_masked_write_bounds_guard_band(offset):
+    """Q = 80 (a partial 128-query tile): guard bands around out keep their sentinel, for the
+    plain and the chunked form."""
+    inp, cfg, _ = _small(61)
+    starts = torch.tensor([5, 40], dtype=torch.int32, device=DEV) if offset else None
+    mask = sa.topk_bitmask_build(inp["topk_idxs"], cfg.KV, key_starts=starts)
+    n = cfg.B * cfg.Q * cfg.H * cfg.Dv
+    buf = torch.full((n + 2 * 4096,), 3.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[4096:4096 + n].view(cfg.B, cfg.Q, cfg.H, cfg.Dv)
+    fn = sa.masked_attn_offset if offset else sa.masked_attn
+    fn(inp["q"], inp["k"], inp["v"], mask, inp["scale"], out=out)
+    torch.cuda.synchronize()
+    assert (buf[:4096] == 3.0).all() and (buf[4096 + n:] == 3.0).all()
+    assert not (out == 3.0).all(dim=-1).any(), "a row of out was not written"
+
+
+def test_masked_graph_replay_tracks_new_masks(oracle_impl):
+    """Capture one call, replay it with new queries and new mask bits: every replay matches
+    the oracle (the launch depends only on the shapes)."""
+    inp, cfg, _ = _small(62)
+    mask = _oracle_mask(oracle_impl, inp["topk_idxs"], cfg.KV)
+    out = torch.empty((cfg.B, cfg.Q, cfg.H, cfg.Dv), dtype=torch.bfloat16, device=DEV)
+    sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"], out=out)  # warm up outside the graph
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"], out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        new = wl.masked_inputs("masked_small", 200 + rep, DEV)
+        inp["q"].copy_(new["q"])
+        mask.copy_(_oracle_mask(oracle_impl, new["topk_idxs"], cfg.KV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = _ref(oracle_impl, inp, mask).reshape(cfg.B, cfg.Q, cfg.H, cfg.Dv)
+        assert_close(to64(out), ref, f"masked replay {rep}")
