@@ -88,7 +88,7 @@ def sdpa_with_sink(qv, keys, sink_value, scale):
 
 # --------------------------------------------------------------------------- sparse_attn pins
 def check_loop_semantics(o):
-    """north star (a): the oracle equals the pages' loop on tiny inputs, with and without
+    """The oracle equals the pages' loop (section 5.2) on tiny inputs, with and without
     duplicate slots."""
     q, kv, sink, idx = _tiny(seed=1)
     scale = 16 ** -0.5
@@ -103,7 +103,7 @@ def check_loop_semantics(o):
 
 
 def check_all_invalid_zero(o):
-    """north star (b): every slot -1 with finite sinks gives exactly 0."""
+    """Every slot -1 with finite sinks gives exactly 0."""
     q, kv, sink, idx = _tiny(seed=2)
     idx[:] = -1
     got = _run_sparse(o, q, kv, sink, idx, 0.25)
@@ -111,7 +111,7 @@ def check_all_invalid_zero(o):
 
 
 def check_order_invariance(o):
-    """north star (c): permuting the K slots leaves the output unchanged."""
+    """Permuting the K slots leaves the output unchanged."""
     q, kv, sink, idx = _tiny(seed=3)
     g = torch.Generator().manual_seed(33)
     perm = torch.randperm(idx.shape[-1], generator=g)
@@ -121,7 +121,7 @@ def check_order_invariance(o):
 
 
 def check_dense_equivalence(o):
-    """north star (d): sink -inf and the full index set reduce to dense softmax attention
+    """Sink -inf and the full index set reduce to dense softmax attention
     (torch scaled_dot_product_attention, float64)."""
     B, S, H, D, T = 1, 3, 4, 16, 24
     g = torch.Generator().manual_seed(4)
@@ -268,7 +268,7 @@ def check_out_of_range_is_empty(o):
 
 # --------------------------------------------------------------------------- bitmask pins
 def check_mask_worked_example(o):
-    """north star (e) and the page's printed example: (2,129,129) -> (2,256,8) with and
+    """The page's printed example: (2,129,129) -> (2,256,8) with and
     without the reserved word; 129 keys -> 8 words; indices {0,128} -> row [1,0,0,0,1,0,0,0]
     with the padding kept."""
     with open(os.path.join(GOLDEN, "bitmask_worked_example.json")) as f:
