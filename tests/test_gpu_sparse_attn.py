@@ -258,3 +258,15 @@ def test_split_then_merge_equals_one_call(splits):
     sa.sparse_attn_merge(*args, out=b, num_splits=splits, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_split_merge_many_tokens(oracle_impl):
+    """4100 tokens with 2 splits (8200 partial blocks, D = 64), tokens sampled at both ends."""
+    B, S, H, D, T, K = 1, 4100, 16, 64, 300, 64
+    inp = _custom(B, S, H, D, T, K, seed=53)
+    out = _run(inp, num_splits=2)
+    torch.cuda.synchronize()
+    tokens = np.array([0, 1, 2047, 4095, 4096, 4099])
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"], tokens)
+    got = to64(out.reshape(B * S, H, D)[torch.as_tensor(tokens, device=DEV)])
+    assert_close(got, ref, "4100 tokens, 2 splits")

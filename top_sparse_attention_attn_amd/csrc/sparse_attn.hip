@@ -458,6 +458,11 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     }
   }
 
+  // Lane-dependent values of the epilogue are rebuilt from the lane id (kept opaque), so none
+  // of them is carried, or spilled, across the tile loop.
+  unsigned lne = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(lne));
+  const int lanee = (int)lne, ge = lanee >> 4, l16e = lanee & 15;
   // Per-head output factor f (score waves own the heads): with no split the sink is folded
   // in, o = O 2^(m-M) / (l 2^(m-M) + 2^(sink-M)); with splits each split keeps its own
   // normalised output O / l (bf16) and lse = m + log2(l), merged afterwards with the sink.
@@ -465,7 +470,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 #pragma unroll
     for (int qi = 0; qi < QB; qi++) {
       if (qi >= nq) break;
-      const int h = (sw + 4 * qi) * 16 + l16;
+      const int h = (sw + 4 * qi) * 16 + l16e;
       const float m = sm.mref[h];
       const float l = sm.lsum[h];
       float f = 0.f, lse = kNegInf;
@@ -490,7 +495,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         f = 1.f / l;
         lse = m + __builtin_log2f(l);
       }
-      if (g == 0) {
+      if (ge == 0) {
         sm.fin[h] = f;
         sm.lsef[h] = lse;
       }
@@ -501,7 +506,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 
   // ---- stage this split's output in the row ring as bf16 with the factor applied:
   //   no split: rows [h][D + 16] of the final output;
-  //   splits:   the MFMA layout [head block][d block][lane][4 heads] of the normalised partial.
+  //   splits:   the MFMA layout [head block][d block][lanee][4 heads] of the normalised partial.
   __bf16* const stg = (__bf16*)&sm.kv[0][0];
   constexpr int kOS = D + 16;  // staged row stride (bf16): 8 banks of skew per row
   static_assert(HP * kOS * 2 <= (int)sizeof(sm.kv) && HP * D * 2 <= (int)sizeof(sm.kv), "staging exceeds the ring");
@@ -511,18 +516,18 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
       for (int hb = 0; hb < HB; hb++) {
         float f[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) f[i] = sm.fin[hb * 16 + 4 * g + i];
+        for (int i = 0; i < 4; i++) f[i] = sm.fin[hb * 16 + 4 * ge + i];
 #pragma unroll
         for (int db = 0; db < NB; db++) {
           if (nsplit == 1) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
-              stg[(hb * 16 + 4 * g + i) * kOS + (db0 + db) * 16 + l16] = (__bf16)(oacc[hb][db][i] * f[i]);
+              stg[(hb * 16 + 4 * ge + i) * kOS + (db0 + db) * 16 + l16e] = (__bf16)(oacc[hb][db][i] * f[i]);
           } else {
             bf16x4 v;
 #pragma unroll
             for (int i = 0; i < 4; i++) v[i] = (__bf16)(oacc[hb][db][i] * f[i]);
-            *(bf16x4*)(&stg[((hb * G::kNDB + db0 + db) * 64 + lane) * 4]) = v;
+            *(bf16x4*)(&stg[((hb * G::kNDB + db0 + db) * 64 + lanee) * 4]) = v;
           }
         }
       }
