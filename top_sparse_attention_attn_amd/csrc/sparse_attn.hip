@@ -504,12 +504,39 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   wait_lgkm0();
   wg_barrier();  // every wave is past its last tile: the row ring is free for staging
 
-  // ---- stage this split's output in the row ring as bf16 with the factor applied:
-  //   no split: rows [h][D + 16] of the final output;
-  //   splits:   the MFMA layout [head block][d block][lanee][4 heads] of the normalised partial.
+  const int tid = threadIdx.x;
+  if (nsplit > 1) {
+    // split partial: the normalised block in the MFMA layout [head block][d block][lane][4 heads]
+    // (8 bytes per lane, 512 contiguous bytes per wave store) straight from the accumulators,
+    // and the log-sum-exps; merged with the other splits of the token (and the sink) by
+    // sparse_attn_combine_kernel
+    if constexpr (NB > 0) {
+      if (pv_active) {
+        __bf16* const wpart = ws_o + (size_t)pair * HP * D;
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++) {
+          float f[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) f[i] = sm.fin[hb * 16 + 4 * ge + i];
+#pragma unroll
+          for (int db = 0; db < NB; db++) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[i] = (__bf16)(oacc[hb][db][i] * f[i]);
+            *(bf16x4*)(wpart + ((hb * G::kNDB + db0 + db) * 64 + lanee) * 4) = v;
+          }
+        }
+      }
+    }
+    if (tid < HP) ws_lse[(size_t)pair * HP + tid] = sm.lsef[tid];
+    return;
+  }
+
+  // ---- no split: stage the final rows [h][D + 16] in the row ring as bf16 with the factor
+  // applied, then store them with 16-byte writes
   __bf16* const stg = (__bf16*)&sm.kv[0][0];
   constexpr int kOS = D + 16;  // staged row stride (bf16): 8 banks of skew per row
-  static_assert(HP * kOS * 2 <= (int)sizeof(sm.kv) && HP * D * 2 <= (int)sizeof(sm.kv), "staging exceeds the ring");
+  static_assert(HP * kOS * 2 <= (int)sizeof(sm.kv), "staging exceeds the ring");
   if constexpr (NB > 0) {
     if (pv_active) {
 #pragma unroll
@@ -518,37 +545,20 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 #pragma unroll
         for (int i = 0; i < 4; i++) f[i] = sm.fin[hb * 16 + 4 * ge + i];
 #pragma unroll
-        for (int db = 0; db < NB; db++) {
-          if (nsplit == 1) {
+        for (int db = 0; db < NB; db++)
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-              stg[(hb * 16 + 4 * ge + i) * kOS + (db0 + db) * 16 + l16e] = (__bf16)(oacc[hb][db][i] * f[i]);
-          } else {
-            bf16x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; i++) v[i] = (__bf16)(oacc[hb][db][i] * f[i]);
-            *(bf16x4*)(&stg[((hb * G::kNDB + db0 + db) * 64 + lanee) * 4]) = v;
-          }
-        }
+          for (int i = 0; i < 4; i++)
+            stg[(hb * 16 + 4 * ge + i) * kOS + (db0 + db) * 16 + l16e] = (__bf16)(oacc[hb][db][i] * f[i]);
       }
     }
   }
   wait_lgkm0();
   wg_barrier();
-  const int tid = threadIdx.x;
-  if (nsplit == 1) {  // final rows, 16-byte stores
-    constexpr int kRC = D / 8;
-    for (int c = tid; c < HP * kRC; c += kThreads) {
-      const int r = c / kRC, k = c % kRC;
-      if (r < H) *(uint4*)(out + ((size_t)tok * H + r) * D + 8 * k) = *(const uint4*)(&stg[r * kOS + 8 * k]);
-    }
-    return;
+  constexpr int kRC = D / 8;
+  for (int c = tid; c < HP * kRC; c += kThreads) {
+    const int r = c / kRC, k = c % kRC;
+    if (r < H) *(uint4*)(out + ((size_t)tok * H + r) * D + 8 * k) = *(const uint4*)(&stg[r * kOS + 8 * k]);
   }
-  // split partial: the normalised block in MFMA layout and the log-sum-exps, merged with the
-  // other splits of the token (and the sink) by sparse_attn_combine_kernel
-  __bf16* const wpart = ws_o + (size_t)pair * HP * D;
-  for (int c = tid; c < HP * D / 8; c += kThreads) ((uint4*)wpart)[c] = ((const uint4*)stg)[c];
-  if (tid < HP) ws_lse[(size_t)pair * HP + tid] = sm.lsef[tid];
 }
 
 template <int D, int HB, bool F8>
