@@ -125,11 +125,13 @@ __device__ __forceinline__ float xor_shuffle(float v, int mask) {
 // (VALU only). permlane32_swap of a register with itself yields, in some order, the
 // values of lanes l and l^32; permlane16_swap likewise for l and l^16. Max and sum are
 // symmetric, so the order does not matter and all four lanes end with the same result.
+// The maximum is IEEE maximum (NaN-propagating, v_maximum3_f32): unlike fmaxf it needs no
+// canonicalising moves of the swapped values.
 __device__ __forceinline__ float max4_x16_x32(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum4_x16_x32(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -397,7 +397,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
               for (int i = 0; i < 4; i++) {
                 const float v = (vg & (1u << (16 * jb + i))) ? sacc[qi][jb][i] * scale_log2 : kNegInf;
                 sacc[qi][jb][i] = v;
-                tmax = fmaxf(tmax, v);
+                tmax = __builtin_elementwise_maximum(tmax, v);
               }
             tmax = max4_x16_x32(tmax);
             const float mold = mst[qi];
@@ -407,7 +407,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
             const bool resc = move && (mold > kNegInf);
             any_resc |= resc;
             const float msub = (mnew > kNegInf) ? mnew : 0.f;  // no finite logit yet: all weights 0
-            float lsum = 0.f;
+            float lsum;
             // this lane's weights for rows 4g+i and 16+4g+i go to P columns 8g .. 8g+7
             bf16x2 pk[4];
 #pragma unroll
@@ -416,7 +416,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 #pragma unroll
               for (int i = 0; i < 4; i++) {
                 pw[i] = exp2_fast(sacc[qi][jb][i] - msub);
-                lsum += pw[i];
+                lsum = (jb == 0 && i == 0) ? pw[0] : lsum + pw[i];  // no 0 + x to start the sum
               }
               pk[2 * jb] = __builtin_convertvector((f32x2){pw[0], pw[1]}, bf16x2);
               pk[2 * jb + 1] = __builtin_convertvector((f32x2){pw[2], pw[3]}, bf16x2);
