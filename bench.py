@@ -38,7 +38,10 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warm-up steps (default: at least 1000 steps and at least "
+                        "--warmup-seconds of them, so the GPU reaches its steady clocks)")
+    p.add_argument("--warmup-seconds", type=float, default=1.5)
     p.add_argument("--config", default="decode", choices=["decode", "decode_fp8", "prefill", "ragged", "masked", "bitmask", "tiny",
                                                         "candidate", "candidate_long"])
     p.add_argument("--sets", type=int, default=NSETS)
@@ -291,8 +294,16 @@ def main():
             sample_desc = "one full step"
         extra_cfg = {"B": cfg.B, "Q": cfg.Q, "KV": cfg.KV, "H": cfg.H}
 
-    for i in range(args.warmup):
-        step(i)
+    if args.warmup is not None:
+        for i in range(args.warmup):
+            step(i)
+    else:  # run warm-up steps until both the step and the time floor are met
+        args.warmup, t0 = 0, time.perf_counter()
+        while args.warmup < 1000 or time.perf_counter() - t0 < args.warmup_seconds:
+            for _ in range(100):
+                step(args.warmup)
+                args.warmup += 1
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
