@@ -13,26 +13,31 @@
 // (v_alignbit) into the tile's 64 bits.
 //
 // Decomposition: one workgroup of 8 waves per (batch, head, 128 queries), in two roles that
-// run one 64-key tile apart, as in the sparse kernel:
-//  * score waves 0-3 each own 32 queries: S^T = K Q^T with the queries in registers (MFMA
-//    16x16x32 bf16), the mask, and the online softmax; the weights go to LDS in exactly the
-//    layout the PV MFMA reads them (one 16-byte chunk per lane), with a lazily moved
-//    reference maximum whose rare moves are passed on as per-query factors;
-//  * value waves 4-7 own the same 32 queries each: they copy the next key/value tile and the
-//    mask words it needs from HBM into LDS, and add P V for the previous tile, V read with
-//    the transposing LDS read. The copies are buffer loads that write LDS directly, the
-//    padded LDS tile filled as one contiguous byte range, 64 lanes x 16 bytes per load: a
-//    lane whose 16 bytes fall in a row's padding, or in a row past KV, gets an offset beyond
-//    the buffer's range, so the hardware reads nothing for it (44 loads per tile). They are
-//    waited for only at the next tile's barrier, so the P V work overlaps their latency.
+// run one 64-key tile apart, as in the sparse kernel. Each wave owns 64 queries (one query half)
+// and one 32-key half of every tile, so each K and V element is read from LDS twice per 128
+// queries (once per query half), and every K or V operand read feeds four MFMAs:
+//  * score waves 0-3 (query half w & 1, key half w >> 1): S^T = K Q^T with the 64 queries in
+//    registers (MFMA 16x16x32 bf16), the mask, and an online softmax over their key half only
+//    (its own lazily moved reference maximum and row sum); the weights go to LDS in exactly the
+//    layout the PV MFMA reads them (one 16-byte chunk per lane), rare reference moves as
+//    per-query factors;
+//  * value waves 4-7 (the same query and key halves): they copy the next key/value tile and the
+//    mask words it needs from HBM into LDS, and add P V of their key half for the previous
+//    tile, V read with the transposing LDS read. The copies are buffer loads that write LDS
+//    directly, the padded LDS tile filled as one contiguous byte range, 64 lanes x 16 bytes per
+//    load: a lane whose 16 bytes fall in a row's padding, or in a row past KV, gets an offset
+//    beyond the buffer's range, so the hardware reads nothing for it (44 loads per tile). They
+//    are waited for only at the next tile's barrier, so the P V work overlaps their latency.
+// The two key halves are two independent softmax splits of the keys; after the last tile they
+// are merged once per query through LDS (o = (2^(m0-M) O0 + 2^(m1-M) O1) / (2^(m0-M) l0 +
+// 2^(m1-M) l1), M = max(m0, m1)).
 // The workgroups of one (batch, head) walk the same tiles at about the same time, so without
 // help each of them would wait for the first one's HBM misses on every tile: the score waves
 // therefore touch the tile kPrefetch tiles ahead (4 bytes per 128-byte line, each workgroup
 // a 1/nqt share of the lines) to bring it into L2 early. Those loads write a scratch LDS
 // word and are waited for only at the end, so they never stall a wave.
-// Each K and V element is read from LDS once per 32 queries. The row strides (416 and 288
-// bytes) and the row order of the transposed reads were chosen with the LDS bank-conflict
-// counter. One barrier per tile.
+// The row strides (416 and 288 bytes) and the row order of the transposed reads were chosen
+// with the LDS bank-conflict counter. One barrier per tile.
 #include "common.h"
 
 namespace sa {
@@ -49,45 +54,50 @@ template <int DQK, int DV>
 struct Smem {
   static constexpr int KS = DQK * 2 + 32;  // K row stride (bytes)
   static constexpr int VS = DV * 2 + 32;   // V row stride (bytes)
-  unsigned char k[2][kKT * KS];            // K tiles t, t+1
-  unsigned char v[3][kKT * VS];            // V tiles t-1, t, t+1
-  bf16x8 p[2][4][2][2][64];                // weights: [tile parity][score wave][query block][32-key step][lane]
+  unsigned char k[2][kKT * KS];            // K tiles t (QK), t+1 (being copied)
+  unsigned char v[2][kKT * VS];            // V tiles t-2 (P V), t-1 (being copied)
+  bf16x8 p[2][4][4][64];                   // weights: [tile parity][score wave][query block][lane]
   uint32_t mw[2][kQT * 4];                 // mask words: [chunk parity][query][4], or [tile parity][query][2]
   uint32_t sink[2][64];                    // destination of the L2 prefetch loads (never read)
-  float alpha[2][4][32];                   // rescale factor per query of the tile (if moved)
-  float fin[kQT];                          // 1 / row sum per query
+  float alpha[2][4][64];                   // rescale factor per query of the tile (if moved)
+  float mref[2][kQT];                      // per key half: final reference maximum per query
+  float lsum[2][kQT];                      // per key half: final weight sum per query
+  float fin[2][kQT];                       // per key half: output factor per query
   int flag[2][4];                          // any rescale in this score wave's queries
 };
 
 }  // namespace masked
 
-template <int DQK, int DV, int MASKBITS, bool OFFSET>
-__global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const uint32_t* __restrict__ mask, __bf16* __restrict__ out, int Q, int KV, int H, int padded_q, int words,
-    int nxcc, float scale_log2) {
+// One role's side of the workgroup (score waves: SCORE; value waves: !SCORE). The roles share the
+// barrier sequence; each keeps only its own registers (queries or accumulators).
+template <int DQK, int DV, int MASKBITS, bool OFFSET, bool SCORE>
+__device__ __forceinline__ void masked_role(masked::Smem<DQK, DV>& sm, const __bf16* __restrict__ q,
+                                            const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                                            const uint32_t* __restrict__ mask, __bf16* __restrict__ out, int Q,
+                                            int KV, int H, int padded_q, int words, int nxcc, float scale_log2) {
   using namespace masked;
   using SM = Smem<DQK, DV>;
   constexpr int KS = SM::KS, VS = SM::VS;
   constexpr int DSTEPS = DQK / 32;  // QK steps over the head dimension
   constexpr int NDB = DV / 16;      // PV output column blocks
   constexpr int KLANES = DQK / 8, VLANES = DV / 8;  // 16-byte chunks per row
+  constexpr int QB = 4;             // 16-query blocks per wave (64 queries)
   static_assert(KLANES <= 64 && VLANES <= 64 && DQK % 32 == 0 && DV % 16 == 0, "head dims");
-  __shared__ __attribute__((aligned(16))) SM sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const bool score = wave < 4;
-  const int pw = score ? wave : wave - 4;  // index of the query group (32 queries) of this wave
+  constexpr bool score = SCORE;
+  const int pw = score ? wave : wave - 4;  // index within the role
+  const int qh = pw & 1, kh = pw >> 1;     // query half (64 queries) and key half (32 keys of a tile)
 
   const int nqt = (Q + kQT - 1) / kQT;
   const int wg = xcd_local_id(blockIdx.x, gridDim.x, nxcc);
   const int qt = wg % nqt;
   const int bh = wg / nqt;
   const int h = bh % H, b = bh / H;
-  const int qbase = qt * kQT + pw * 32;  // first query of this wave's group
+  const int qbase = qt * kQT + qh * 64;  // first query of this wave's half
   const int nkt = (KV + kKT - 1) / kKT;
 
   // chunked-context form: the clamped start and the first position past the bit words
@@ -98,15 +108,21 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     ksc = ks < pmax ? ks : pmax;
   }
 
-  // ---- score waves: queries (B operand), mask rows, softmax state
-  bf16x8 qreg[2][DSTEPS];
-  bool qlive[2] = {false, false};
-  float m_ref[2] = {kNegInf, kNegInf}, l_part[2] = {0.f, 0.f};
-  if (score) {
+  // ---- score waves: queries (B operand), softmax state of this key half
+  bf16x8 qreg[QB][SCORE ? DSTEPS : 1];
+  bool qlive[QB];
+  float m_ref[QB], l_part[QB];
 #pragma unroll
-    for (int qb = 0; qb < 2; qb++) {
+  for (int qb = 0; qb < QB; qb++) {
+    const int qr = qbase + 16 * qb + l16;
+    qlive[qb] = qr < Q;
+    m_ref[qb] = kNegInf;
+    l_part[qb] = 0.f;
+  }
+  if constexpr (SCORE) {
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++) {
       const int qr = qbase + 16 * qb + l16;
-      qlive[qb] = qr < Q;
 #pragma unroll
       for (int s = 0; s < DSTEPS; s++) {
         bf16x8 z = {};
@@ -115,44 +131,53 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     }
   }
 
-  // ---- value waves: output accumulators O[query 4g+i of block qb][column 16 db + l16]
-  f32x4 oacc[2][NDB];
+  // ---- value waves: output accumulators O[query 4g+i of block qb][column 16 db + l16] of this
+  // key half
+  constexpr int NDBX = SCORE ? 1 : NDB;
+  f32x4 oacc[QB][NDBX];
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++)
+  for (int qb = 0; qb < QB; qb++)
 #pragma unroll
-    for (int db = 0; db < NDB; db++) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < NDBX; db++) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Tile copy by the value waves. The K tile in LDS is KCH 16-byte chunks per row (KLANES of
-  // data, then padding), 64 rows: KCH loads of 64 chunks each; V likewise with VCH. Load n of
-  // the NGI per tile belongs to wave 4 + n % 4; a lane's byte offset is taken relative to row 0
-  // of the tile (head h), kOob for a padding chunk. The offsets are recomputed per tile rather
-  // than kept, to leave the registers to the score path.
-  constexpr int KCH = KS / 16, VCH = VS / 16, NGI = KCH + VCH, GPW = (NGI + 3) / 4;
-  auto chunk_off = [&](int n, int ln) -> uint32_t {
-    if (n < KCH) {
-      const int c = 64 * n + ln, r = c / KCH, col = c % KCH;
-      return col < KLANES ? (uint32_t)(r * H * DQK * 2 + col * 16) : kOob;
+  // Tile copies by the value waves: K of tile t one tile before its QK, V of tile t one tile
+  // before its P V (which runs two tiles after its QK). The K tile in LDS is KCH 16-byte chunks
+  // per row (KLANES of data, then padding), 64 rows: KCH loads of 64 chunks each; V likewise
+  // with VCH. Load n belongs to wave 4 + n % 4; a lane's byte offset is taken relative to row 0
+  // of the tile (head h), kOob for a padding chunk. The offsets do not depend on the tile: the
+  // value waves compute theirs once (12 registers) and the tile only moves the buffer's base.
+  constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 3) / 4, VM = (VCH + 3) / 4;
+  uint32_t koffs[SCORE ? 1 : KM], voffs[SCORE ? 1 : VM];
+  if constexpr (!SCORE) {
+#pragma unroll
+    for (int m = 0; m < KM; m++) {
+      const int c = 64 * (pw + 4 * m) + lane, r = c / KCH, col = c % KCH;
+      koffs[m] = col < KLANES ? (uint32_t)(r * H * DQK * 2 + col * 16) : kOob;
     }
-    const int c = 64 * (n - KCH) + ln, r = c / VCH, col = c % VCH;
-    return col < VLANES ? (uint32_t)(r * H * DV * 2 + col * 16) : kOob;
-  };
-  auto gather = [&](int t) {
+#pragma unroll
+    for (int m = 0; m < VM; m++) {
+      const int c = 64 * (pw + 4 * m) + lane, r = c / VCH, col = c % VCH;
+      voffs[m] = col < VLANES ? (uint32_t)(r * H * DV * 2 + col * 16) : kOob;
+    }
+  }
+  auto gather_k = [&](int t) {
     // rows t*kKT + r with r < nv are in range; the range ends inside row nv's first byte
     const int nv = min(KV - t * kKT, kKT);
     const size_t row0 = ((size_t)b * KV + (size_t)t * kKT) * H + h;
     const u32x4 kr = buffer_rsrc(k + row0 * DQK, (uint32_t)(((nv - 1) * H + 1) * DQK * 2));
-    const u32x4 vr = buffer_rsrc(v + row0 * DV, (uint32_t)(((nv - 1) * H + 1) * DV * 2));
-    const uint32_t kd = lds_addr(sm.k[t & 1]), vd = lds_addr(sm.v[t % 3]);
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // keeps the offsets inside the loop (not hoisted into registers)
+    const uint32_t kd = lds_addr(sm.k[t & 1]);
 #pragma unroll
-    for (int m = 0; m < GPW; m++) {
-      const int n = pw + 4 * m;
-      if (n < KCH)
-        dma_lds16(kr, chunk_off(n, ln), kd + 1024 * n);
-      else if (n < NGI)
-        dma_lds16(vr, chunk_off(n, ln), vd + 1024 * (n - KCH));
-    }
+    for (int m = 0; m < KM; m++)
+      if (pw + 4 * m < KCH) dma_lds16(kr, koffs[m % (SCORE ? 1 : KM)], kd + 1024 * (pw + 4 * m));
+  };
+  auto gather_v = [&](int t) {
+    const int nv = min(KV - t * kKT, kKT);
+    const size_t row0 = ((size_t)b * KV + (size_t)t * kKT) * H + h;
+    const u32x4 vr = buffer_rsrc(v + row0 * DV, (uint32_t)(((nv - 1) * H + 1) * DV * 2));
+    const uint32_t vd = lds_addr(sm.v[t & 1]);
+#pragma unroll
+    for (int m = 0; m < VM; m++)
+      if (pw + 4 * m < VCH) dma_lds16(vr, voffs[m % (SCORE ? 1 : VM)], vd + 1024 * (pw + 4 * m));
   };
 
   // Mask copy by the value waves, for tile t: the wide form copies the 4 words of keys
@@ -213,94 +238,115 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   }
   wait_lgkm0();
   wg_barrier();
-  if (!score && nkt > 0) {
-    gather(0);
-    mask_copy(0);
-  }
-  if (score)
+  if (!SCORE && nkt > 0) gather_k(0);
+  if (SCORE)
     for (int t = 1; t < kPrefetch && t < nkt; t++) prefetch(t);
 
-  for (int t = 0; t <= nkt; t++) {
-    if (score) wait_lgkm0();
-    else wait_vm_lgkm0<0>();  // this wave's rows of tile t have landed
-    wg_barrier();             // tile t and P(t-1) visible; everyone is done with tile t-2 and P(t-2)
-    if (!score && t + 1 < nkt) {
-      gather(t + 1);
-      mask_copy(t + 1);
-    }
-
-    if (score && t < nkt) {
-      const int par = t & 1;
-      // this tile's two mask words per query block (copied in by the value waves)
-      uint32_t mwd[2][2];
+  // Software pipeline over the tiles, one barrier per step: at step t the score waves compute
+  // QK of tile t and, interleaved with its MFMAs, the softmax of tile t-1 (its logits kept in
+  // registers from the previous step), while the value waves copy K of tile t+1, V of tile t-1
+  // and the mask words of tile t, and add P V of tile t-2. Steps run t = 0 .. nkt + 1 (rounded
+  // up to an even count; the work of a step outside the tiles is skipped or, in the score waves,
+  // masked to nothing), unrolled by two so each step's buffer parity is a constant.
+  f32x4 sacc[2][QB][2];  // score waves: logits of tiles t (parity t & 1) and t - 1
+  auto step = [&](const int t, const int par) __attribute__((always_inline)) {  // par == (t & 1)
+    if (SCORE) wait_lgkm0();
+    else wait_vm_lgkm0<0>();  // this wave's copies of the previous step have landed
+    // K(t), V(t-2), P(t-2), the mask words of tile t-1 and the softmax factors of tile t-2 are
+    // visible; everyone is done with K(t-1), V(t-3), P(t-3) and the mask words of tile t-2
+    wg_barrier();
+    if constexpr (!SCORE) {
+      if (t + 1 < nkt) gather_k(t + 1);
+      if (t >= 1 && t - 1 < nkt) gather_v(t - 1);
+      if (t < nkt) mask_copy(t);
+      if (t >= 2 && t - 2 < nkt) {  // O += P V of this key half for tile t-2
+        const int pp = par;         // parity of tile t-2
+        if (sm.flag[pp][pw]) {
 #pragma unroll
-      for (int qb = 0; qb < 2; qb++) {
-        const int ql = pw * 32 + 16 * qb + l16;
-        if constexpr (OFFSET) {
-          // bits of positions p0 .. p0 + 63, none at or past pmax
-          const uint4 x = *(const uint4*)&sm.mw[t & 1][ql * 4];
-          const uint32_t p0 = 64u * (uint32_t)t + ksc, sh = p0 & 31u;
-          const int rem = (int)pmax - (int)p0;
-          const uint32_t lim0 = rem >= 32 ? ~0u : (rem > 0 ? (1u << rem) - 1u : 0u);
-          const uint32_t lim1 = rem >= 64 ? ~0u : (rem > 32 ? (1u << (rem - 32)) - 1u : 0u);
-          mwd[qb][0] = qlive[qb] ? __builtin_amdgcn_alignbit(x.y, x.x, sh) & lim0 : 0u;
-          mwd[qb][1] = qlive[qb] ? __builtin_amdgcn_alignbit(x.z, x.y, sh) & lim1 : 0u;
-        } else if (mask == nullptr) {
-          mwd[qb][0] = mwd[qb][1] = qlive[qb] ? ~0u : 0u;
-        } else {
-          const uint2 x = MASKBITS == 128 ? *(const uint2*)&sm.mw[(t >> 1) & 1][ql * 4 + 2 * (t & 1)]
-                                          : *(const uint2*)&sm.mw[t & 1][ql * 2];
-          mwd[qb][0] = qlive[qb] ? x.x : 0u;
-          mwd[qb][1] = qlive[qb] ? x.y : 0u;
+          for (int qb = 0; qb < QB; qb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const float a = sm.alpha[pp][pw][16 * qb + 4 * g + i];
+#pragma unroll
+              for (int db = 0; db < NDBX; db++) oacc[qb][db][i] *= a;
+            }
         }
+        const int r4 = (lane >> 2) & 3, c4 = lane & 3;
+        const unsigned char* vk = sm.v[pp] + (32 * kh + 4 * g + r4) * VS + 8 * c4;
+        bf16x8 pa[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; qb++) pa[qb] = sm.p[pp][pw][qb][lane];
+#pragma unroll
+        for (int db = 0; db < NDB; db++) {
+          const bf16x8 bv = concat_tr(lds_read_tr16(vk + 32 * db), lds_read_tr16(vk + 16 * VS + 32 * db));
+#pragma unroll
+          for (int qb = 0; qb < QB; qb++) oacc[qb][db % NDBX] = mfma16x16x32(pa[qb], bv, oacc[qb][db % NDBX]);
+        }
+      }
+    } else {
+      const int ts = t - 1;  // tile of this step's softmax (parity par ^ 1)
+      const bool ts_live = ts >= 0 && ts < nkt;
+      // the softmax tile's mask word (32 keys of this key half) per query block
+      uint32_t mwd[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; qb++) {
+        const int ql = qh * 64 + 16 * qb + l16;
+        uint32_t wv;
+        if constexpr (OFFSET) {
+          // bits of positions p0 + 32 kh .. p0 + 32 kh + 31, none at or past pmax
+          const uint4 x = *(const uint4*)&sm.mw[par ^ 1][ql * 4];
+          const uint32_t p0 = 64u * (uint32_t)ts + ksc, sh = p0 & 31u;
+          const int rem = (int)pmax - (int)p0 - 32 * kh;
+          const uint32_t lim = rem >= 32 ? ~0u : (rem > 0 ? (1u << rem) - 1u : 0u);
+          wv = (kh == 0 ? __builtin_amdgcn_alignbit(x.y, x.x, sh) : __builtin_amdgcn_alignbit(x.z, x.y, sh)) & lim;
+        } else if (mask == nullptr) {
+          wv = ~0u;
+        } else {
+          wv = MASKBITS == 128 ? sm.mw[(ts >> 1) & 1][ql * 4 + 2 * (ts & 1) + kh] : sm.mw[par ^ 1][ql * 2 + kh];
+        }
+        mwd[qb] = (qlive[qb] && ts_live) ? wv : 0u;
       }
       // keys past KV (last tile only)
-      const int nvalid = KV - t * kKT;
-      const uint32_t kv0 = nvalid >= 32 ? ~0u : ((1u << nvalid) - 1u);
-      const uint32_t kv1 = nvalid >= 64 ? ~0u : (nvalid > 32 ? ((1u << (nvalid - 32)) - 1u) : 0u);
+      const int nvalid = KV - ts * kKT - 32 * kh;
+      const uint32_t kvm = nvalid >= 32 ? ~0u : (nvalid > 0 ? ((1u << nvalid) - 1u) : 0u);
 
-      // ---- S^T = K Q^T: 4 key blocks x 2 query blocks, each K operand feeding both
-      const unsigned char* kb = sm.k[t & 1] + l16 * KS + 16 * g;
-      f32x4 sacc[2][4];
+      // ---- S^T = K Q^T of tile t: 2 key blocks x 4 query blocks, each K operand feeding all
+      // four (on stale K when t >= nkt: those logits are masked out at the next step)
+      const unsigned char* kb = sm.k[par] + (32 * kh + l16) * KS + 16 * g;
 #pragma unroll
-      for (int qb = 0; qb < 2; qb++)
+      for (int qb = 0; qb < QB; qb++) sacc[par][qb][0] = sacc[par][qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      constexpr int NK = 2 * DSTEPS;  // K operands: (key block, step) pairs
+      constexpr int KR = 4;           // K operands in flight
+      auto kop = [&](int n) { return *(const bf16x8*)(kb + (n % 2) * 16 * KS + 64 * (n / 2)); };
+      bf16x8 ka[KR];
 #pragma unroll
-        for (int j = 0; j < 4; j++) sacc[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      constexpr int NK = 4 * DSTEPS;  // K operands: (key block, step) pairs
-      auto kop = [&](int n) { return *(const bf16x8*)(kb + (n % 4) * 16 * KS + 64 * (n / 4)); };
-      bf16x8 ka[4];
-#pragma unroll
-      for (int n = 0; n < 4; n++) ka[n] = kop(n);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      for (int n = 0; n < KR; n++) ka[n] = kop(n);
 #pragma unroll
       for (int n = 0; n < NK; n++) {
-        const int jb = n % 4, st = n / 4;
-        sacc[0][jb] = mfma16x16x32(ka[n % 4], qreg[0][st], sacc[0][jb]);
-        sacc[1][jb] = mfma16x16x32(ka[n % 4], qreg[1][st], sacc[1][jb]);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (n + 4 < NK) {
-          ka[n % 4] = kop(n + 4);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+        const int jb = n % 2, st = n / 2;
+#pragma unroll
+        for (int qb = 0; qb < QB; qb++)
+          sacc[par][qb][jb] = mfma16x16x32(ka[n % KR], qreg[qb][st % (SCORE ? DSTEPS : 1)], sacc[par][qb][jb]);
+        if (n + KR < NK) ka[n % KR] = kop(n + KR);
       }
-      __builtin_amdgcn_sched_barrier(0);
 
-      // ---- online softmax per query block; lane holds keys 16 jb + 4 g + i of query l16
+      // ---- online softmax of tile t-1 per query block over this key half; lane holds keys
+      // 16 jb + 4 g + i of query l16. Branch free (stores by all lanes of a query), so that it
+      // interleaves with the MFMAs above.
+      const int sp = par ^ 1;
       bool any_resc = false;
 #pragma unroll
-      for (int qb = 0; qb < 2; qb++) {
-        const uint32_t w0 = mwd[qb][0] & kv0, w1 = mwd[qb][1] & kv1;
-        const uint32_t vg0 = w0 >> (4 * g), vg1 = w1 >> (4 * g);
+      for (int qb = 0; qb < QB; qb++) {
+        const uint32_t vg = (mwd[qb] & kvm) >> (4 * g);
         float tmax = kNegInf;
 #pragma unroll
-        for (int jb = 0; jb < 4; jb++)
+        for (int jb = 0; jb < 2; jb++)
 #pragma unroll
           for (int i = 0; i < 4; i++) {
-            const uint32_t vgw = (jb < 2) ? vg0 : vg1;
-            const bool vis = (vgw >> (16 * (jb & 1) + i)) & 1u;
-            const float x = vis ? sacc[qb][jb][i] * scale_log2 : kNegInf;
-            sacc[qb][jb][i] = x;
-            tmax = fmaxf(tmax, x);
+            const bool vis = (vg >> (16 * jb + i)) & 1u;
+            const float x = vis ? sacc[sp][qb][jb][i] * scale_log2 : kNegInf;
+            sacc[sp][qb][jb][i] = x;  // in place: tile t-1's logits are dead after this step
+            tmax = __builtin_elementwise_maximum(tmax, x);
           }
         tmax = max4_x16_x32(tmax);
         const float mold = m_ref[qb];
@@ -311,87 +357,109 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
         any_resc |= resc;
         m_ref[qb] = mnew;
         const float msub = (mnew > kNegInf) ? mnew : 0.f;  // no visible key yet: all weights 0
-        float lsum = 0.f;
+        // MFMA k index 8g+i = key 4g + i (i < 4) or 16 + 4g + i - 4 of this key half
+        float lsum;
+        bf16x2 pk[4];
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-          // MFMA k index 8g+i = key 32 ks + 4g + i (i < 4) or 32 ks + 16 + 4g + i - 4
-          bf16x2 pk[4];
-#pragma unroll
-          for (int hf = 0; hf < 2; hf++) {
-            float pv[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              pv[i] = exp2_fast(sacc[qb][2 * ks + hf][i] - msub);
-              lsum += pv[i];
-            }
-            pk[2 * hf] = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
-            pk[2 * hf + 1] = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
-          }
-          sm.p[par][pw][qb][ks][lane] =
-              bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
-        }
-        l_part[qb] = l_part[qb] * alpha + lsum;
-        if (g == 0) sm.alpha[par][pw][16 * qb + l16] = resc ? alpha : 1.f;
-      }
-      if (lane == 0) sm.flag[par][pw] = __any(any_resc) ? 1 : 0;
-      if (t + kPrefetch < nkt) prefetch(t + kPrefetch);
-    }
-
-    // ---- value waves: O += P V for tile t-1
-    if (!score && t >= 1) {
-      const int tp = t - 1, par = tp & 1;
-      if (sm.flag[par][pw]) {
-#pragma unroll
-        for (int qb = 0; qb < 2; qb++)
+        for (int hf = 0; hf < 2; hf++) {
+          float pv[4];
 #pragma unroll
           for (int i = 0; i < 4; i++) {
-            const float a = sm.alpha[par][pw][16 * qb + 4 * g + i];
-#pragma unroll
-            for (int db = 0; db < NDB; db++) oacc[qb][db][i] *= a;
+            pv[i] = exp2_fast(sacc[sp][qb][hf][i] - msub);
+            lsum = (hf == 0 && i == 0) ? pv[0] : lsum + pv[i];
           }
-      }
-      const int r4 = (lane >> 2) & 3, c4 = lane & 3;
-      const unsigned char* vb = sm.v[tp % 3] + (4 * g + r4) * VS + 8 * c4;
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        const bf16x8 pa0 = sm.p[par][pw][0][ks][lane];
-        const bf16x8 pa1 = sm.p[par][pw][1][ks][lane];
-        const unsigned char* vk = vb + 32 * ks * VS;
-#pragma unroll
-        for (int db = 0; db < NDB; db++) {
-          const bf16x8 bv = concat_tr(lds_read_tr16(vk + 32 * db), lds_read_tr16(vk + 16 * VS + 32 * db));
-          oacc[0][db] = mfma16x16x32(pa0, bv, oacc[0][db]);
-          oacc[1][db] = mfma16x16x32(pa1, bv, oacc[1][db]);
+          pk[2 * hf] = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
+          pk[2 * hf + 1] = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
         }
+        sm.p[sp][pw][qb][lane] = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
+        l_part[qb] = l_part[qb] * alpha + lsum;
+        sm.alpha[sp][pw][16 * qb + l16] = resc ? alpha : 1.f;  // the 4 lanes of a query agree
       }
+      sm.flag[sp][pw] = __any(any_resc) ? 1 : 0;  // every lane stores the same value
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + kPrefetch < nkt) prefetch(t + kPrefetch);
     }
+  };
+  const int nsteps = (nkt + 3) & ~1;  // t = 0 .. nkt + 1, rounded up to an even count
+  for (int t = 0; t < nsteps; t += 2) {
+    step(t, 0);
+    step(t + 1, 1);
   }
 
-  // ---- normalise: row sums per query (score waves), 1/l to LDS, then the value waves
-  // scale and store (queries past Q are not written)
+  // ---- merge the two key halves and store. Score waves publish each query's reference maximum
+  // and weight sum of their key half; each query's factors f_kh = 2^(m_kh - M) / L follow,
+  // L = sum over the halves of 2^(m_kh - M) l_kh, M = max(m_0, m_1) (f = 0 without any visible
+  // key). Value waves of key half 1 leave f_1 O_1 in LDS, those of key half 0 add f_0 O_0,
+  // round once and store (queries past Q are not written).
   if (score) {
 #pragma unroll
-    for (int qb = 0; qb < 2; qb++) {
+    for (int qb = 0; qb < QB; qb++) {
       const float l = sum4_x16_x32(l_part[qb]);
-      if (g == 0) sm.fin[pw * 32 + 16 * qb + l16] = l > 0.f ? 1.f / l : 0.f;
+      if (g == 0) {
+        sm.mref[kh][qh * 64 + 16 * qb + l16] = m_ref[qb];
+        sm.lsum[kh][qh * 64 + 16 * qb + l16] = l;
+      }
     }
   }
   wait_vm_lgkm0<0>();
   wg_barrier();
-  if (!score) {
+  if (tid < kQT) {
+    const float m0 = sm.mref[0][tid], m1 = sm.mref[1][tid];
+    const float M = __builtin_elementwise_maximum(m0, m1);
+    const float c0 = m0 > kNegInf ? exp2_fast(m0 - M) : 0.f, c1 = m1 > kNegInf ? exp2_fast(m1 - M) : 0.f;
+    const float L = c0 * sm.lsum[0][tid] + c1 * sm.lsum[1][tid];
+    sm.fin[0][tid] = L > 0.f ? c0 / L : 0.f;
+    sm.fin[1][tid] = L > 0.f ? c1 / L : 0.f;
+  }
+  wait_lgkm0();
+  wg_barrier();  // factors ready; every wave is past its last tile, so the tile buffers are free
+  // f_1 O_1 of query half qh, in the accumulator layout [qb][db][lane] (fp32), over the tile buffers
+  f32x4* const xch = (f32x4*)&sm.k[0][0];
+  static_assert(2 * QB * NDB * 64 * 16 <= (int)(sizeof(SM::k) + sizeof(SM::v)), "merge exceeds the tile buffers");
+  if (!SCORE && kh == 1) {
 #pragma unroll
-    for (int qb = 0; qb < 2; qb++)
+    for (int qb = 0; qb < QB; qb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float f = sm.fin[1][qh * 64 + 16 * qb + 4 * g + i];
+#pragma unroll
+        for (int db = 0; db < NDBX; db++) oacc[qb][db][i] *= f;
+      }
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++)
+#pragma unroll
+      for (int db = 0; db < NDBX; db++) xch[((qh * QB + qb) * NDB + db) * 64 + lane] = oacc[qb][db];
+  }
+  wait_lgkm0();
+  wg_barrier();
+  if (!SCORE && kh == 0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int ql = 16 * qb + 4 * g + i;
         const int qo = qbase + ql;
-        if (qo >= Q) continue;
-        const float f = sm.fin[pw * 32 + ql];
+        const float f = sm.fin[0][qh * 64 + ql];
         __bf16* orow = out + (((size_t)b * Q + qo) * H + h) * DV + l16;
 #pragma unroll
-        for (int db = 0; db < NDB; db++) orow[db * 16] = (__bf16)(oacc[qb][db][i] * f);
+        for (int db = 0; db < NDBX; db++) {
+          const float o = __builtin_fmaf(oacc[qb][db][i], f, xch[((qh * QB + qb) * NDB + db) * 64 + lane][i]);
+          if (qo < Q) orow[db * 16] = (__bf16)o;
+        }
       }
   }
+}
+
+template <int DQK, int DV, int MASKBITS, bool OFFSET>
+__global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const uint32_t* __restrict__ mask, __bf16* __restrict__ out, int Q, int KV, int H, int padded_q, int words,
+    int nxcc, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) masked::Smem<DQK, DV> sm;
+  if (threadIdx.x < 256)  // waves 0-3
+    masked_role<DQK, DV, MASKBITS, OFFSET, true>(sm, q, k, v, mask, out, Q, KV, H, padded_q, words, nxcc, scale_log2);
+  else
+    masked_role<DQK, DV, MASKBITS, OFFSET, false>(sm, q, k, v, mask, out, Q, KV, H, padded_q, words, nxcc, scale_log2);
 }
 
 // XCDs of the current device (workgroups are dispatched round-robin over them).
