@@ -12,30 +12,25 @@
 // waves copy three words per query with 4-byte loads and the score waves funnel-shift them
 // (v_alignbit) into the tile's 64 bits.
 //
-// Decomposition: one workgroup of 8 waves per (batch, head, 128 queries), in two roles that
-// run one 64-key tile apart, as in the sparse kernel. Each wave owns 64 queries (one query half)
-// and one 32-key half of every tile, so each K and V element is read from LDS twice per 128
-// queries (once per query half), and every K or V operand read feeds four MFMAs:
-//  * score waves 0-3 (query half w & 1, key half w >> 1): S^T = K Q^T with the 64 queries in
-//    registers (MFMA 16x16x32 bf16), the mask, and an online softmax over their key half only
-//    (its own lazily moved reference maximum and row sum); the weights go to LDS in exactly the
-//    layout the PV MFMA reads them (one 16-byte chunk per lane), rare reference moves as
-//    per-query factors;
-//  * value waves 4-7 (the same query and key halves): they copy the next key/value tile and the
-//    mask words it needs from HBM into LDS, and add P V of their key half for the previous
-//    tile, V read with the transposing LDS read. The copies are buffer loads that write LDS
-//    directly, the padded LDS tile filled as one contiguous byte range, 64 lanes x 16 bytes per
-//    load: a lane whose 16 bytes fall in a row's padding, or in a row past KV, gets an offset
-//    beyond the buffer's range, so the hardware reads nothing for it (44 loads per tile). They
-//    are waited for only at the next tile's barrier, so the P V work overlaps their latency.
-// The two key halves are two independent softmax splits of the keys; after the last tile they
-// are merged once per query through LDS (o = (2^(m0-M) O0 + 2^(m1-M) O1) / (2^(m0-M) l0 +
-// 2^(m1-M) l1), M = max(m0, m1)).
+// Decomposition: one workgroup of 8 waves per (batch, head, 128 queries), 64-key tiles. All waves
+// do the same work: wave w owns 32 queries (quarter w & 3) and one 32-key half (w >> 2) of every
+// tile, and computes S^T = K Q^T with its queries in registers (MFMA 16x16x32 bf16), the mask,
+// an online softmax over its key half (own lazily moved reference maximum and row sum), and
+// O += P V with the weights kept in registers (a lane's 8 logits of a query are exactly its P
+// operand of the P V MFMA) and V read with the transposing LDS read. With two such waves per
+// SIMD, one wave's softmax (VALU work) runs beside the other's MFMAs. The two key halves are two
+// independent softmax splits of the keys, merged once per query through LDS after the last tile
+// (o = (2^(m0-M) O0 + 2^(m1-M) O1) / (2^(m0-M) l0 + 2^(m1-M) l1), M = max(m0, m1)).
+// The waves share the copies of the next key/value tile and its mask words from HBM into LDS:
+// buffer loads that write LDS directly, the padded LDS tile filled as one contiguous byte range,
+// 64 lanes x 16 bytes per load: a lane whose 16 bytes fall in a row's padding, or in a row past
+// KV, gets an offset beyond the buffer's range, so the hardware reads nothing for it (44 loads
+// per tile). They are waited for only at the next tile's barrier.
 // The workgroups of one (batch, head) walk the same tiles at about the same time, so without
-// help each of them would wait for the first one's HBM misses on every tile: the score waves
+// help each of them would wait for the first one's HBM misses on every tile: waves 0 and 1
 // therefore touch the tile kPrefetch tiles ahead (4 bytes per 128-byte line, each workgroup
 // a 1/nqt share of the lines) to bring it into L2 early. Those loads write a scratch LDS
-// word and are waited for only at the end, so they never stall a wave.
+// word and are waited for only at the next barrier, so they never stall a wave.
 // The row strides (416 and 288 bytes) and the row order of the transposed reads were chosen
 // with the LDS bank-conflict counter. One barrier per tile.
 #include "common.h"
@@ -54,50 +49,45 @@ template <int DQK, int DV>
 struct Smem {
   static constexpr int KS = DQK * 2 + 32;  // K row stride (bytes)
   static constexpr int VS = DV * 2 + 32;   // V row stride (bytes)
-  unsigned char k[2][kKT * KS];            // K tiles t (QK), t+1 (being copied)
-  unsigned char v[2][kKT * VS];            // V tiles t-2 (P V), t-1 (being copied)
-  bf16x8 p[2][4][4][64];                   // weights: [tile parity][score wave][query block][lane]
+  unsigned char k[2][kKT * KS];            // K tiles t (in use), t+1 (being copied)
+  unsigned char v[2][kKT * VS];            // V tiles t (in use), t+1 (being copied)
   uint32_t mw[2][kQT * 4];                 // mask words: [chunk parity][query][4], or [tile parity][query][2]
   uint32_t sink[2][64];                    // destination of the L2 prefetch loads (never read)
-  float alpha[2][4][64];                   // rescale factor per query of the tile (if moved)
+  float alpha[8][2][16];                   // per wave: rescale factor per query of a moved reference
   float mref[2][kQT];                      // per key half: final reference maximum per query
   float lsum[2][kQT];                      // per key half: final weight sum per query
   float fin[2][kQT];                       // per key half: output factor per query
-  int flag[2][4];                          // any rescale in this score wave's queries
 };
 
 }  // namespace masked
 
-// One role's side of the workgroup (score waves: SCORE; value waves: !SCORE). The roles share the
-// barrier sequence; each keeps only its own registers (queries or accumulators).
-template <int DQK, int DV, int MASKBITS, bool OFFSET, bool SCORE>
-__device__ __forceinline__ void masked_role(masked::Smem<DQK, DV>& sm, const __bf16* __restrict__ q,
-                                            const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-                                            const uint32_t* __restrict__ mask, __bf16* __restrict__ out, int Q,
-                                            int KV, int H, int padded_q, int words, int nxcc, float scale_log2) {
+template <int DQK, int DV, int MASKBITS, bool OFFSET>
+__global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const uint32_t* __restrict__ mask, __bf16* __restrict__ out, int Q, int KV, int H, int padded_q, int words,
+    int nxcc, float scale_log2) {
   using namespace masked;
   using SM = Smem<DQK, DV>;
   constexpr int KS = SM::KS, VS = SM::VS;
   constexpr int DSTEPS = DQK / 32;  // QK steps over the head dimension
   constexpr int NDB = DV / 16;      // PV output column blocks
   constexpr int KLANES = DQK / 8, VLANES = DV / 8;  // 16-byte chunks per row
-  constexpr int QB = 4;             // 16-query blocks per wave (64 queries)
+  constexpr int QB = 2;             // 16-query blocks per wave (32 queries)
   static_assert(KLANES <= 64 && VLANES <= 64 && DQK % 32 == 0 && DV % 16 == 0, "head dims");
+  __shared__ __attribute__((aligned(16))) SM sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  constexpr bool score = SCORE;
-  const int pw = score ? wave : wave - 4;  // index within the role
-  const int qh = pw & 1, kh = pw >> 1;     // query half (64 queries) and key half (32 keys of a tile)
+  const int qq = wave & 3, kh = wave >> 2;  // query quarter (32 queries) and key half (32 keys of a tile)
 
   const int nqt = (Q + kQT - 1) / kQT;
   const int wg = xcd_local_id(blockIdx.x, gridDim.x, nxcc);
   const int qt = wg % nqt;
   const int bh = wg / nqt;
   const int h = bh % H, b = bh / H;
-  const int qbase = qt * kQT + qh * 64;  // first query of this wave's half
+  const int qbase = qt * kQT + qq * 32;  // first query of this wave's quarter
   const int nkt = (KV + kKT - 1) / kKT;
 
   // chunked-context form: the clamped start and the first position past the bit words
@@ -108,8 +98,9 @@ __device__ __forceinline__ void masked_role(masked::Smem<DQK, DV>& sm, const __b
     ksc = ks < pmax ? ks : pmax;
   }
 
-  // ---- score waves: queries (B operand), softmax state of this key half
-  bf16x8 qreg[QB][SCORE ? DSTEPS : 1];
+  // ---- queries (B operand of QK), softmax state of this key half, output accumulators
+  // O[query 4g+i of block qb][column 16 db + l16] of this key half
+  bf16x8 qreg[QB][DSTEPS];
   bool qlive[QB];
   float m_ref[QB], l_part[QB];
 #pragma unroll
@@ -118,77 +109,60 @@ __device__ __forceinline__ void masked_role(masked::Smem<DQK, DV>& sm, const __b
     qlive[qb] = qr < Q;
     m_ref[qb] = kNegInf;
     l_part[qb] = 0.f;
-  }
-  if constexpr (SCORE) {
 #pragma unroll
-    for (int qb = 0; qb < QB; qb++) {
-      const int qr = qbase + 16 * qb + l16;
-#pragma unroll
-      for (int s = 0; s < DSTEPS; s++) {
-        bf16x8 z = {};
-        qreg[qb][s] = qlive[qb] ? *(const bf16x8*)(q + (((size_t)b * Q + qr) * H + h) * DQK + 32 * s + 8 * g) : z;
-      }
+    for (int s = 0; s < DSTEPS; s++) {
+      bf16x8 z = {};
+      qreg[qb][s] = qlive[qb] ? *(const bf16x8*)(q + (((size_t)b * Q + qr) * H + h) * DQK + 32 * s + 8 * g) : z;
     }
   }
-
-  // ---- value waves: output accumulators O[query 4g+i of block qb][column 16 db + l16] of this
-  // key half
-  constexpr int NDBX = SCORE ? 1 : NDB;
-  f32x4 oacc[QB][NDBX];
+  f32x4 oacc[QB][NDB];
 #pragma unroll
   for (int qb = 0; qb < QB; qb++)
 #pragma unroll
-    for (int db = 0; db < NDBX; db++) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < NDB; db++) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Tile copies by the value waves: K of tile t one tile before its QK, V of tile t one tile
-  // before its P V (which runs two tiles after its QK). The K tile in LDS is KCH 16-byte chunks
-  // per row (KLANES of data, then padding), 64 rows: KCH loads of 64 chunks each; V likewise
-  // with VCH. Load n belongs to wave 4 + n % 4; a lane's byte offset is taken relative to row 0
-  // of the tile (head h), kOob for a padding chunk. The offsets do not depend on the tile: the
-  // value waves compute theirs once (12 registers) and the tile only moves the buffer's base.
-  constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 3) / 4, VM = (VCH + 3) / 4;
-  uint32_t koffs[SCORE ? 1 : KM], voffs[SCORE ? 1 : VM];
-  if constexpr (!SCORE) {
+  // Tile copies, shared by all 8 waves: the K tile in LDS is KCH 16-byte chunks per row (KLANES
+  // of data, then padding), 64 rows: KCH loads of 64 chunks each; V likewise with VCH. Load n
+  // belongs to wave n % 8; a lane's byte offset is taken relative to row 0 of the tile (head h),
+  // kOob for a padding chunk. The offsets do not depend on the tile: each wave computes its own
+  // once and the tile only moves the buffer's base.
+  constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 7) / 8, VM = (VCH + 7) / 8;
+  uint32_t koffs[KM], voffs[VM];
 #pragma unroll
-    for (int m = 0; m < KM; m++) {
-      const int c = 64 * (pw + 4 * m) + lane, r = c / KCH, col = c % KCH;
-      koffs[m] = col < KLANES ? (uint32_t)(r * H * DQK * 2 + col * 16) : kOob;
-    }
-#pragma unroll
-    for (int m = 0; m < VM; m++) {
-      const int c = 64 * (pw + 4 * m) + lane, r = c / VCH, col = c % VCH;
-      voffs[m] = col < VLANES ? (uint32_t)(r * H * DV * 2 + col * 16) : kOob;
-    }
+  for (int m = 0; m < KM; m++) {
+    const int c = 64 * (wave + 8 * m) + lane, r = c / KCH, col = c % KCH;
+    koffs[m] = col < KLANES ? (uint32_t)(r * H * DQK * 2 + col * 16) : kOob;
   }
-  auto gather_k = [&](int t) {
+#pragma unroll
+  for (int m = 0; m < VM; m++) {
+    const int c = 64 * (wave + 8 * m) + lane, r = c / VCH, col = c % VCH;
+    voffs[m] = col < VLANES ? (uint32_t)(r * H * DV * 2 + col * 16) : kOob;
+  }
+  auto gather = [&](int t) {
     // rows t*kKT + r with r < nv are in range; the range ends inside row nv's first byte
     const int nv = min(KV - t * kKT, kKT);
     const size_t row0 = ((size_t)b * KV + (size_t)t * kKT) * H + h;
     const u32x4 kr = buffer_rsrc(k + row0 * DQK, (uint32_t)(((nv - 1) * H + 1) * DQK * 2));
-    const uint32_t kd = lds_addr(sm.k[t & 1]);
+    const u32x4 vr = buffer_rsrc(v + row0 * DV, (uint32_t)(((nv - 1) * H + 1) * DV * 2));
+    const uint32_t kd = lds_addr(sm.k[t & 1]), vd = lds_addr(sm.v[t & 1]);
 #pragma unroll
     for (int m = 0; m < KM; m++)
-      if (pw + 4 * m < KCH) dma_lds16(kr, koffs[m % (SCORE ? 1 : KM)], kd + 1024 * (pw + 4 * m));
-  };
-  auto gather_v = [&](int t) {
-    const int nv = min(KV - t * kKT, kKT);
-    const size_t row0 = ((size_t)b * KV + (size_t)t * kKT) * H + h;
-    const u32x4 vr = buffer_rsrc(v + row0 * DV, (uint32_t)(((nv - 1) * H + 1) * DV * 2));
-    const uint32_t vd = lds_addr(sm.v[t & 1]);
+      if (wave + 8 * m < KCH) dma_lds16(kr, koffs[m], kd + 1024 * (wave + 8 * m));
 #pragma unroll
     for (int m = 0; m < VM; m++)
-      if (pw + 4 * m < VCH) dma_lds16(vr, voffs[m % (SCORE ? 1 : VM)], vd + 1024 * (pw + 4 * m));
+      if (wave + 8 * m < VCH) dma_lds16(vr, voffs[m], vd + 1024 * (wave + 8 * m));
   };
 
-  // Mask copy by the value waves, for tile t: the wide form copies the 4 words of keys
+  // Mask copy for tile t, by waves 4-7 (pw = 0..3): the wide form copies the 4 words of keys
   // [128 c, 128 c + 128) of all kQT queries at the even tile t = 2c (two 16-byte loads, by waves
   // 4 and 5), into sm.mw[c & 1][query][4]; the control form copies the 2 words of tile t (four
-  // 4-byte loads, by waves 4-7) into sm.mw[t & 1][query][2]; the chunked form copies words
-  // w0 .. w0 + 3 of mask position 64 t + key_start (eight 4-byte loads) into
-  // sm.mw[t & 1][query][4]. Rows past padded_q read nothing.
+  // 4-byte loads) into sm.mw[t & 1][query][2]; the chunked form copies words w0 .. w0 + 3 of mask
+  // position 64 t + key_start (eight 4-byte loads) into sm.mw[t & 1][query][4]. Rows past
+  // padded_q read nothing.
   const int q0 = qt * kQT;
   auto mask_copy = [&](int t) {
-    if (mask == nullptr) return;
+    if (mask == nullptr || wave < 4) return;
+    const int pw = wave - 4;
     const u32x4 mr = buffer_rsrc(mask + ((size_t)b * padded_q + q0) * words,
                                  (uint32_t)(min(kQT, padded_q - q0) * words * 4));
     if constexpr (OFFSET) {
@@ -208,24 +182,26 @@ __device__ __forceinline__ void masked_role(masked::Smem<DQK, DV>& sm, const __b
     }
   };
 
-  // L2 prefetch of tile t by the score waves: 128-byte line L of the K tile (row L / LK, part
-  // L % LK) is touched by the workgroup with qt = L % nqt, by score wave 0; the V tile's lines
-  // by score wave 1. Rows past KV are out of the buffer's range and read nothing.
+  // L2 prefetch of tile t by waves 0 (K) and 1 (V): 128-byte line L of the tile (row L / LR,
+  // part L % LR) is touched by the workgroup with qt = L % nqt. Rows past KV are out of the
+  // buffer's range and read nothing. Returns the loads issued.
   constexpr int LK = DQK * 2 / 128, LV = DV * 2 / 128;
   static_assert(DQK * 2 % 128 == 0 && DV * 2 % 128 == 0, "rows are whole 128-byte lines");
-  auto prefetch = [&](int t) {
-    if (pw >= 2) return;
+  auto prefetch = [&](int t) -> int {
+    if (wave >= 2) return 0;
     const int nv = min(KV - t * kKT, kKT);
     const size_t row0 = ((size_t)b * KV + (size_t)t * kKT) * H + h;
-    const int LR = pw == 0 ? LK : LV, nlines = kKT * LR;
-    const u32x4 rs = pw == 0 ? buffer_rsrc(k + row0 * DQK, (uint32_t)(((nv - 1) * H + 1) * DQK * 2))
-                             : buffer_rsrc(v + row0 * DV, (uint32_t)(((nv - 1) * H + 1) * DV * 2));
-    const int rowb = pw == 0 ? H * DQK * 2 : H * DV * 2;
-    for (int j0 = 0; qt + nqt * j0 < nlines; j0 += 64) {
+    const int LR = wave == 0 ? LK : LV, nlines = kKT * LR;
+    const u32x4 rs = wave == 0 ? buffer_rsrc(k + row0 * DQK, (uint32_t)(((nv - 1) * H + 1) * DQK * 2))
+                               : buffer_rsrc(v + row0 * DV, (uint32_t)(((nv - 1) * H + 1) * DV * 2));
+    const int rowb = wave == 0 ? H * DQK * 2 : H * DV * 2;
+    int n = 0;
+    for (int j0 = 0; qt + nqt * j0 < nlines; j0 += 64, n++) {
       const int L = qt + nqt * (j0 + lane);
       const uint32_t off = L < nlines ? (uint32_t)((L / LR) * rowb + (L % LR) * 128) : kOob;
-      dma_lds4(rs, off, lds_addr(sm.sink[pw]));
+      dma_lds4(rs, off, lds_addr(sm.sink[wave]));
     }
+    return n;
   };
 
   // The tiles start zeroed: if a skipped (out-of-range) chunk leaves LDS untouched, the rows past
@@ -238,168 +214,159 @@ __device__ __forceinline__ void masked_role(masked::Smem<DQK, DV>& sm, const __b
   }
   wait_lgkm0();
   wg_barrier();
-  if (!SCORE && nkt > 0) gather_k(0);
-  if (SCORE)
-    for (int t = 1; t < kPrefetch && t < nkt; t++) prefetch(t);
-
-  // Software pipeline over the tiles, one barrier per step: at step t the score waves compute
-  // QK of tile t and, interleaved with its MFMAs, the softmax of tile t-1 (its logits kept in
-  // registers from the previous step), while the value waves copy K of tile t+1, V of tile t-1
-  // and the mask words of tile t, and add P V of tile t-2. Steps run t = 0 .. nkt + 1 (rounded
-  // up to an even count; the work of a step outside the tiles is skipped or, in the score waves,
-  // masked to nothing), unrolled by two so each step's buffer parity is a constant.
-  f32x4 sacc[2][QB][2];  // score waves: logits of tiles t (parity t & 1) and t - 1
-  auto step = [&](const int t, const int par) __attribute__((always_inline)) {  // par == (t & 1)
-    if (SCORE) wait_lgkm0();
-    else wait_vm_lgkm0<0>();  // this wave's copies of the previous step have landed
-    // K(t), V(t-2), P(t-2), the mask words of tile t-1 and the softmax factors of tile t-2 are
-    // visible; everyone is done with K(t-1), V(t-3), P(t-3) and the mask words of tile t-2
-    wg_barrier();
-    if constexpr (!SCORE) {
-      if (t + 1 < nkt) gather_k(t + 1);
-      if (t >= 1 && t - 1 < nkt) gather_v(t - 1);
-      if (t < nkt) mask_copy(t);
-      if (t >= 2 && t - 2 < nkt) {  // O += P V of this key half for tile t-2
-        const int pp = par;         // parity of tile t-2
-        if (sm.flag[pp][pw]) {
-#pragma unroll
-          for (int qb = 0; qb < QB; qb++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const float a = sm.alpha[pp][pw][16 * qb + 4 * g + i];
-#pragma unroll
-              for (int db = 0; db < NDBX; db++) oacc[qb][db][i] *= a;
-            }
-        }
-        const int r4 = (lane >> 2) & 3, c4 = lane & 3;
-        const unsigned char* vk = sm.v[pp] + (32 * kh + 4 * g + r4) * VS + 8 * c4;
-        bf16x8 pa[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; qb++) pa[qb] = sm.p[pp][pw][qb][lane];
-#pragma unroll
-        for (int db = 0; db < NDB; db++) {
-          const bf16x8 bv = concat_tr(lds_read_tr16(vk + 32 * db), lds_read_tr16(vk + 16 * VS + 32 * db));
-#pragma unroll
-          for (int qb = 0; qb < QB; qb++) oacc[qb][db % NDBX] = mfma16x16x32(pa[qb], bv, oacc[qb][db % NDBX]);
-        }
-      }
-    } else {
-      const int ts = t - 1;  // tile of this step's softmax (parity par ^ 1)
-      const bool ts_live = ts >= 0 && ts < nkt;
-      // the softmax tile's mask word (32 keys of this key half) per query block
-      uint32_t mwd[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++) {
-        const int ql = qh * 64 + 16 * qb + l16;
-        uint32_t wv;
-        if constexpr (OFFSET) {
-          // bits of positions p0 + 32 kh .. p0 + 32 kh + 31, none at or past pmax
-          const uint4 x = *(const uint4*)&sm.mw[par ^ 1][ql * 4];
-          const uint32_t p0 = 64u * (uint32_t)ts + ksc, sh = p0 & 31u;
-          const int rem = (int)pmax - (int)p0 - 32 * kh;
-          const uint32_t lim = rem >= 32 ? ~0u : (rem > 0 ? (1u << rem) - 1u : 0u);
-          wv = (kh == 0 ? __builtin_amdgcn_alignbit(x.y, x.x, sh) : __builtin_amdgcn_alignbit(x.z, x.y, sh)) & lim;
-        } else if (mask == nullptr) {
-          wv = ~0u;
-        } else {
-          wv = MASKBITS == 128 ? sm.mw[(ts >> 1) & 1][ql * 4 + 2 * (ts & 1) + kh] : sm.mw[par ^ 1][ql * 2 + kh];
-        }
-        mwd[qb] = (qlive[qb] && ts_live) ? wv : 0u;
-      }
-      // keys past KV (last tile only)
-      const int nvalid = KV - ts * kKT - 32 * kh;
-      const uint32_t kvm = nvalid >= 32 ? ~0u : (nvalid > 0 ? ((1u << nvalid) - 1u) : 0u);
-
-      // ---- S^T = K Q^T of tile t: 2 key blocks x 4 query blocks, each K operand feeding all
-      // four (on stale K when t >= nkt: those logits are masked out at the next step)
-      const unsigned char* kb = sm.k[par] + (32 * kh + l16) * KS + 16 * g;
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++) sacc[par][qb][0] = sacc[par][qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      constexpr int NK = 2 * DSTEPS;  // K operands: (key block, step) pairs
-      constexpr int KR = 4;           // K operands in flight
-      auto kop = [&](int n) { return *(const bf16x8*)(kb + (n % 2) * 16 * KS + 64 * (n / 2)); };
-      bf16x8 ka[KR];
-#pragma unroll
-      for (int n = 0; n < KR; n++) ka[n] = kop(n);
-#pragma unroll
-      for (int n = 0; n < NK; n++) {
-        const int jb = n % 2, st = n / 2;
-#pragma unroll
-        for (int qb = 0; qb < QB; qb++)
-          sacc[par][qb][jb] = mfma16x16x32(ka[n % KR], qreg[qb][st % (SCORE ? DSTEPS : 1)], sacc[par][qb][jb]);
-        if (n + KR < NK) ka[n % KR] = kop(n + KR);
-      }
-
-      // ---- online softmax of tile t-1 per query block over this key half; lane holds keys
-      // 16 jb + 4 g + i of query l16. Branch free (stores by all lanes of a query), so that it
-      // interleaves with the MFMAs above.
-      const int sp = par ^ 1;
-      bool any_resc = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++) {
-        const uint32_t vg = (mwd[qb] & kvm) >> (4 * g);
-        float tmax = kNegInf;
-#pragma unroll
-        for (int jb = 0; jb < 2; jb++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const bool vis = (vg >> (16 * jb + i)) & 1u;
-            const float x = vis ? sacc[sp][qb][jb][i] * scale_log2 : kNegInf;
-            sacc[sp][qb][jb][i] = x;  // in place: tile t-1's logits are dead after this step
-            tmax = __builtin_elementwise_maximum(tmax, x);
-          }
-        tmax = max4_x16_x32(tmax);
-        const float mold = m_ref[qb];
-        const bool move = tmax > mold + 8.0f;  // also true for the first finite maximum
-        const float mnew = move ? tmax : mold;
-        const float alpha = move ? exp2_fast(mold - mnew) : 1.f;  // 0 when mold = -inf
-        const bool resc = move && (mold > kNegInf);
-        any_resc |= resc;
-        m_ref[qb] = mnew;
-        const float msub = (mnew > kNegInf) ? mnew : 0.f;  // no visible key yet: all weights 0
-        // MFMA k index 8g+i = key 4g + i (i < 4) or 16 + 4g + i - 4 of this key half
-        float lsum;
-        bf16x2 pk[4];
-#pragma unroll
-        for (int hf = 0; hf < 2; hf++) {
-          float pv[4];
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            pv[i] = exp2_fast(sacc[sp][qb][hf][i] - msub);
-            lsum = (hf == 0 && i == 0) ? pv[0] : lsum + pv[i];
-          }
-          pk[2 * hf] = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
-          pk[2 * hf + 1] = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
-        }
-        sm.p[sp][pw][qb][lane] = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
-        l_part[qb] = l_part[qb] * alpha + lsum;
-        sm.alpha[sp][pw][16 * qb + l16] = resc ? alpha : 1.f;  // the 4 lanes of a query agree
-      }
-      sm.flag[sp][pw] = __any(any_resc) ? 1 : 0;  // every lane stores the same value
-      __builtin_amdgcn_sched_barrier(0);
-      if (t + kPrefetch < nkt) prefetch(t + kPrefetch);
-    }
-  };
-  const int nsteps = (nkt + 3) & ~1;  // t = 0 .. nkt + 1, rounded up to an even count
-  for (int t = 0; t < nsteps; t += 2) {
-    step(t, 0);
-    step(t + 1, 1);
+  if (nkt > 0) {
+    gather(0);
+    mask_copy(0);
   }
+  // prefetch loads issued after this wave's last tile copies: vector-memory loads complete in
+  // issue order, so the copies have landed once only these may still be outstanding
+  int pf_out = 0;
+  for (int t = 1; t < kPrefetch && t < nkt; t++) pf_out += prefetch(t);
 
-  // ---- merge the two key halves and store. Score waves publish each query's reference maximum
-  // and weight sum of their key half; each query's factors f_kh = 2^(m_kh - M) / L follow,
-  // L = sum over the halves of 2^(m_kh - M) l_kh, M = max(m_0, m_1) (f = 0 without any visible
-  // key). Value waves of key half 1 leave f_1 O_1 in LDS, those of key half 0 add f_0 O_0,
-  // round once and store (queries past Q are not written).
-  if (score) {
+  // The two waves of a SIMD (the key halves of one query quarter) would otherwise run each phase
+  // (QK MFMAs, softmax VALU work, P V MFMAs) at the same time; the key-half-0 wave gets issue
+  // priority, so it runs ahead and each wave's softmax lands beside the other's MFMAs.
+  if (kh == 0) __builtin_amdgcn_s_setprio(2);
+
+  for (int t = 0; t < nkt; t++) {
+    wait_vm_lgkm0_dyn(pf_out);  // this wave's copies of tile t have landed
+    wg_barrier();               // tile t visible; everyone is done with tile t-1's buffers
+    pf_out = 0;
+    if (t + 1 < nkt) {
+      gather(t + 1);
+      mask_copy(t + 1);
+    }
+    const int par = t & 1;
+    // this tile's mask word (32 keys of this key half) per query block
+    uint32_t mwd[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; qb++) {
-      const float l = sum4_x16_x32(l_part[qb]);
-      if (g == 0) {
-        sm.mref[kh][qh * 64 + 16 * qb + l16] = m_ref[qb];
-        sm.lsum[kh][qh * 64 + 16 * qb + l16] = l;
+      const int ql = qq * 32 + 16 * qb + l16;
+      uint32_t wv;
+      if constexpr (OFFSET) {
+        // bits of positions p0 + 32 kh .. p0 + 32 kh + 31, none at or past pmax
+        const uint4 x = *(const uint4*)&sm.mw[par][ql * 4];
+        const uint32_t p0 = 64u * (uint32_t)t + ksc, sh = p0 & 31u;
+        const int rem = (int)pmax - (int)p0 - 32 * kh;
+        const uint32_t lim = rem >= 32 ? ~0u : (rem > 0 ? (1u << rem) - 1u : 0u);
+        wv = (kh == 0 ? __builtin_amdgcn_alignbit(x.y, x.x, sh) : __builtin_amdgcn_alignbit(x.z, x.y, sh)) & lim;
+      } else if (mask == nullptr) {
+        wv = ~0u;
+      } else {
+        wv = MASKBITS == 128 ? sm.mw[(t >> 1) & 1][ql * 4 + 2 * (t & 1) + kh] : sm.mw[par][ql * 2 + kh];
+      }
+      mwd[qb] = qlive[qb] ? wv : 0u;
+    }
+    // keys past KV (last tile only)
+    const int nvalid = KV - t * kKT - 32 * kh;
+    const uint32_t kvm = nvalid >= 32 ? ~0u : (nvalid > 0 ? ((1u << nvalid) - 1u) : 0u);
+
+    // ---- S^T = K Q^T of this key half: 2 key blocks x 2 query blocks, each K operand feeding both
+    const unsigned char* kb = sm.k[par] + (32 * kh + l16) * KS + 16 * g;
+    f32x4 sacc[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++) sacc[qb][0] = sacc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int NK = 2 * DSTEPS;  // K operands: (key block, step) pairs
+    constexpr int KR = 4;           // K operands in flight
+    auto kop = [&](int n) { return *(const bf16x8*)(kb + (n % 2) * 16 * KS + 64 * (n / 2)); };
+    bf16x8 ka[KR];
+#pragma unroll
+    for (int n = 0; n < KR; n++) ka[n] = kop(n);
+    __builtin_amdgcn_sched_group_barrier(0x100, KR, 0);
+#pragma unroll
+    for (int n = 0; n < NK; n++) {
+      const int jb = n % 2, st = n / 2;
+#pragma unroll
+      for (int qb = 0; qb < QB; qb++) sacc[qb][jb] = mfma16x16x32(ka[n % KR], qreg[qb][st], sacc[qb][jb]);
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      if (n + KR < NK) {
+        ka[n % KR] = kop(n + KR);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- online softmax per query block over this key half; lane holds keys 16 jb + 4 g + i of
+    // query l16, and packs its 8 weights as its own P operand of the P V MFMA (k index 8g+i =
+    // key 4g + i for i < 4, 16 + 4g + i - 4 for i >= 4), so P never goes through LDS
+    bf16x8 pop[QB];
+    bool any_resc = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++) {
+      const uint32_t vg = (mwd[qb] & kvm) >> (4 * g);
+      float tmax = kNegInf;
+#pragma unroll
+      for (int jb = 0; jb < 2; jb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const bool vis = (vg >> (16 * jb + i)) & 1u;
+          const float x = vis ? sacc[qb][jb][i] * scale_log2 : kNegInf;
+          sacc[qb][jb][i] = x;
+          tmax = __builtin_elementwise_maximum(tmax, x);
+        }
+      tmax = max4_x16_x32(tmax);
+      const float mold = m_ref[qb];
+      const bool move = tmax > mold + 8.0f;  // also true for the first finite maximum
+      const float mnew = move ? tmax : mold;
+      const float alpha = move ? exp2_fast(mold - mnew) : 1.f;  // 0 when mold = -inf
+      const bool resc = move && (mold > kNegInf);
+      any_resc |= resc;
+      m_ref[qb] = mnew;
+      const float msub = (mnew > kNegInf) ? mnew : 0.f;  // no visible key yet: all weights 0
+      float lsum;
+      bf16x2 pk[4];
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          pv[i] = exp2_fast(sacc[qb][hf][i] - msub);
+          lsum = (hf == 0 && i == 0) ? pv[0] : lsum + pv[i];
+        }
+        pk[2 * hf] = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
+        pk[2 * hf + 1] = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
+      }
+      pop[qb] = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
+      l_part[qb] = l_part[qb] * alpha + lsum;
+      sm.alpha[wave][qb][l16] = resc ? alpha : 1.f;  // the 4 lanes of a query agree
+    }
+    // a moved reference rescales this wave's accumulators; the accumulator lane of query 4g+i
+    // reads that query's factor back from LDS (this wave's own area: no barrier needed)
+    if (__any(any_resc)) {
+      wait_lgkm0();
+#pragma unroll
+      for (int qb = 0; qb < QB; qb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float a = sm.alpha[wave][qb][4 * g + i];
+#pragma unroll
+          for (int db = 0; db < NDB; db++) oacc[qb][db][i] *= a;
+        }
+    }
+
+    // ---- O += P V of this key half: V operands with the transposing read, each feeding both
+    // query blocks
+    const int r4 = (lane >> 2) & 3, c4 = lane & 3;
+    const unsigned char* vk = sm.v[par] + (32 * kh + 4 * g + r4) * VS + 8 * c4;
+#pragma unroll
+    for (int db = 0; db < NDB; db++) {
+      const bf16x8 bv = concat_tr(lds_read_tr16(vk + 32 * db), lds_read_tr16(vk + 16 * VS + 32 * db));
+#pragma unroll
+      for (int qb = 0; qb < QB; qb++) oacc[qb][db] = mfma16x16x32(pop[qb], bv, oacc[qb][db]);
+    }
+    if (t + kPrefetch < nkt) pf_out = prefetch(t + kPrefetch);
+  }
+
+  // ---- merge the two key halves and store. Every wave publishes each query's reference maximum
+  // and weight sum of its key half; each query's factors f_kh = 2^(m_kh - M) / L follow,
+  // L = sum over the halves of 2^(m_kh - M) l_kh, M = max(m_0, m_1) (f = 0 without any visible
+  // key). Waves of key half 1 leave f_1 O_1 in LDS, those of key half 0 add f_0 O_0, round once
+  // and store (queries past Q are not written).
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) {
+    const float l = sum4_x16_x32(l_part[qb]);
+    sm.mref[kh][qq * 32 + 16 * qb + l16] = m_ref[qb];  // the 4 lanes of a query agree
+    sm.lsum[kh][qq * 32 + 16 * qb + l16] = l;
   }
   wait_vm_lgkm0<0>();
   wg_barrier();
@@ -413,53 +380,41 @@ __device__ __forceinline__ void masked_role(masked::Smem<DQK, DV>& sm, const __b
   }
   wait_lgkm0();
   wg_barrier();  // factors ready; every wave is past its last tile, so the tile buffers are free
-  // f_1 O_1 of query half qh, in the accumulator layout [qb][db][lane] (fp32), over the tile buffers
+  // f_1 O_1 of query quarter qq, in the accumulator layout [qb][db][lane] (fp32), over the tile buffers
   f32x4* const xch = (f32x4*)&sm.k[0][0];
-  static_assert(2 * QB * NDB * 64 * 16 <= (int)(sizeof(SM::k) + sizeof(SM::v)), "merge exceeds the tile buffers");
-  if (!SCORE && kh == 1) {
+  static_assert(4 * QB * NDB * 64 * 16 <= (int)(sizeof(SM::k) + sizeof(SM::v)), "merge exceeds the tile buffers");
+  if (kh == 1) {
 #pragma unroll
     for (int qb = 0; qb < QB; qb++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const float f = sm.fin[1][qh * 64 + 16 * qb + 4 * g + i];
+        const float f = sm.fin[1][qq * 32 + 16 * qb + 4 * g + i];
 #pragma unroll
-        for (int db = 0; db < NDBX; db++) oacc[qb][db][i] *= f;
+        for (int db = 0; db < NDB; db++) oacc[qb][db][i] *= f;
       }
 #pragma unroll
     for (int qb = 0; qb < QB; qb++)
 #pragma unroll
-      for (int db = 0; db < NDBX; db++) xch[((qh * QB + qb) * NDB + db) * 64 + lane] = oacc[qb][db];
+      for (int db = 0; db < NDB; db++) xch[((qq * QB + qb) * NDB + db) * 64 + lane] = oacc[qb][db];
   }
   wait_lgkm0();
   wg_barrier();
-  if (!SCORE && kh == 0) {
+  if (kh == 0) {
 #pragma unroll
     for (int qb = 0; qb < QB; qb++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int ql = 16 * qb + 4 * g + i;
         const int qo = qbase + ql;
-        const float f = sm.fin[0][qh * 64 + ql];
+        const float f = sm.fin[0][qq * 32 + ql];
         __bf16* orow = out + (((size_t)b * Q + qo) * H + h) * DV + l16;
 #pragma unroll
-        for (int db = 0; db < NDBX; db++) {
-          const float o = __builtin_fmaf(oacc[qb][db][i], f, xch[((qh * QB + qb) * NDB + db) * 64 + lane][i]);
+        for (int db = 0; db < NDB; db++) {
+          const float o = __builtin_fmaf(oacc[qb][db][i], f, xch[((qq * QB + qb) * NDB + db) * 64 + lane][i]);
           if (qo < Q) orow[db * 16] = (__bf16)o;
         }
       }
   }
-}
-
-template <int DQK, int DV, int MASKBITS, bool OFFSET>
-__global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const uint32_t* __restrict__ mask, __bf16* __restrict__ out, int Q, int KV, int H, int padded_q, int words,
-    int nxcc, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) masked::Smem<DQK, DV> sm;
-  if (threadIdx.x < 256)  // waves 0-3
-    masked_role<DQK, DV, MASKBITS, OFFSET, true>(sm, q, k, v, mask, out, Q, KV, H, padded_q, words, nxcc, scale_log2);
-  else
-    masked_role<DQK, DV, MASKBITS, OFFSET, false>(sm, q, k, v, mask, out, Q, KV, H, padded_q, words, nxcc, scale_log2);
 }
 
 // XCDs of the current device (workgroups are dispatched round-robin over them).
