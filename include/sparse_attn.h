@@ -206,10 +206,16 @@ int masked_attn_fwd(const void* q, const void* k, const void* v, const uint32_t*
  * every bit word gives o = 0. Otherwise as masked_attn_fwd: same arguments
  * (no mask_load_bits: the words of a chunk tile sit at any bit offset and are
  * read 4 bytes at a time), same layouts, no sink, o = 0 for an empty J.
+ * lse        device fp32 [B][Q][H], or NULL: the natural-log log-sum-exp of
+ *            each query's scaled logits over J (-inf for an empty J), so that
+ *            the outputs of the chunks of one context can be merged:
+ *            o = sum_c exp(lse_c - LSE) o_c, LSE = log sum_c exp(lse_c) (the
+ *            fallback from one global mask to per-chunk masks, prhub summary of
+ *            vLLM PR #48770, review discussion). 4-byte aligned.
  * Requires mask != NULL (when B*Q*H > 0), words >= 4, words % 4 == 0,
  * padded_q >= Q; KV is not limited by words. Returns SA_ERR_NULL without a mask.
  */
-int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
+int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, float* lse,
                            int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
                            int64_t words, float scale, void* stream);
 

@@ -153,6 +153,53 @@ def test_offset_start_zero_equals_plain():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("cut", [150, 64, 1])
+def test_offset_chunks_merged_by_lse_equal_global(oracle_impl, cut):
+    """The fallback from one global mask to per-chunk masks (prhub summary of vLLM PR #48770,
+    review discussion): the context cut at `cut` into two chunks, each run through the chunked
+    form with its key_start, merged by the returned log-sum-exps, equals the oracle on the
+    global mask and the global form."""
+    inp, cfg, _ = _small(56)
+    B, KV = cfg.B, cfg.KV
+    gmask = _oracle_mask(oracle_impl, inp["topk_idxs"], KV)
+    glob = sa.masked_attn(inp["q"], inp["k"], inp["v"], gmask, inp["scale"])
+    outs, lses = [], []
+    for start, end in ((0, cut), (cut, KV)):
+        starts = torch.full((B,), start, dtype=torch.int32, device=DEV)
+        cmask = sa.topk_bitmask_build(inp["topk_idxs"], KV, key_starts=starts)
+        k = inp["k"][:, start:end].contiguous()
+        v = inp["v"][:, start:end].contiguous()
+        o, lse = sa.masked_attn_offset(inp["q"], k, v, cmask, inp["scale"], return_lse=True)
+        outs.append(o.double().cpu())
+        lses.append(lse.double().cpu())
+    torch.cuda.synchronize()
+    lse = torch.stack(lses)                                    # [chunk, B, Q, H]
+    w = torch.nan_to_num(torch.exp(lse - torch.logsumexp(lse, dim=0)), nan=0.0)  # no visible key: 0
+    merged = (w[0][..., None] * outs[0] + w[1][..., None] * outs[1]).numpy()
+    ref = _ref(oracle_impl, inp, gmask).reshape(cfg.B, cfg.Q, cfg.H, cfg.Dv)
+    assert_close(merged, ref, f"chunks cut at {cut}, merged by lse")
+    assert_close(merged, to64(glob), f"chunks cut at {cut} vs the global form")
+
+
+def test_offset_lse_closed_forms():
+    """lse of a query with exactly one visible key is that key's scaled logit (the weight sum
+    is exactly 1); without any visible key it is -inf."""
+    inp, cfg, _ = _small(57)
+    B, n = cfg.B, 100
+    k, v = _chunk(inp, 0, n, 58)
+    idx = torch.full_like(inp["topk_idxs"], -1)
+    idx[:, 0::2, 0] = 7  # even queries see key 7 only, odd queries nothing
+    mask = sa.topk_bitmask_build(idx, n, key_starts=torch.zeros(B, dtype=torch.int32, device=DEV))
+    o, lse = sa.masked_attn_offset(inp["q"], k, v, mask, inp["scale"], return_lse=True)
+    torch.cuda.synchronize()
+    want = (inp["q"].double() * k[:, 7].double()[:, None]).sum(-1) * inp["scale"]  # [B, Q, H]
+    got = lse.double()
+    assert torch.isneginf(got[:, 1::2]).all()
+    assert torch.allclose(got[:, 0::2], want[:, 0::2], atol=1e-3, rtol=1e-4)
+    assert torch.equal(o[:, 0::2], v[:, 7][:, None].expand_as(o[:, 0::2]))
+    assert torch.count_nonzero(o[:, 1::2]).item() == 0
+
+
 @pytest.mark.parametrize("start", [37, 64, 200])
 def test_offset_equals_plain_on_shifted_mask(start):
     """A chunk [start, start + n) read through the global mask's offset equals the plain form

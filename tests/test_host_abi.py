@@ -105,8 +105,8 @@ def test_masked_rejects_before_any_hip_call():
     assert _masked(Q=0) == 0
 
 
-def _offset(q=FAKE, k=FAKE, v=FAKE, m=FAKE, o=FAKE, B=1, Q=4, KV=64, H=2, Dqk=192, Dv=128, pq=128, W=8):
-    return _lib().masked_attn_offset_fwd(q, k, v, m, o, B, Q, KV, H, Dqk, Dv, pq, W, 0.1, None)
+def _offset(q=FAKE, k=FAKE, v=FAKE, m=FAKE, o=FAKE, lse=None, B=1, Q=4, KV=64, H=2, Dqk=192, Dv=128, pq=128, W=8):
+    return _lib().masked_attn_offset_fwd(q, k, v, m, o, lse, B, Q, KV, H, Dqk, Dv, pq, W, 0.1, None)
 
 
 def test_masked_offset_rejects_before_any_hip_call():
@@ -118,6 +118,7 @@ def test_masked_offset_rejects_before_any_hip_call():
     assert _offset(o=None) == 1
     assert _offset(v=FAKE_ODD) == 3
     assert _offset(m=FAKE_ODD) == 3
+    assert _offset(lse=ctypes.c_void_p((1 << 20) + 2)) == 3  # lse must be 4-byte aligned
     assert _offset(H=0) == 0
 
 

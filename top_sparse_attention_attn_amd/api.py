@@ -63,7 +63,7 @@ def _load():
         lib.topk_bitmask_build.restype = I
         lib.masked_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, F, I, P]
         lib.masked_attn_fwd.restype = I
-        lib.masked_attn_offset_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, F, P]
+        lib.masked_attn_offset_fwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, F, P]
         lib.masked_attn_offset_fwd.restype = I
         lib.candidate_mask_apply.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P]
         lib.candidate_mask_apply.restype = I
@@ -257,16 +257,20 @@ def masked_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.T
 
 
 def masked_attn_offset(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor, scale: float,
-                       out: torch.Tensor | None = None) -> torch.Tensor:
+                       out: torch.Tensor | None = None, return_lse: bool = False):
     """Chunked-context form: k, v are a chunk of KV keys and chunk key j reads mask bit
     key_start + j, with key_start = mask[b, 0, words-1] (written by topk_bitmask_build from
-    key_starts). Shapes as masked_attn; the mask is required."""
+    key_starts). Shapes as masked_attn; the mask is required. With return_lse, also returns
+    lse [B, Q, H] fp32 (natural log, -inf for no visible key), for merging the chunks of one
+    context: o = sum_c exp(lse_c - LSE) o_c, LSE = logsumexp_c lse_c."""
     if mask is None:
         raise ValueError("masked_attn_offset needs the mask (it carries key_start)")
-    return _masked_call("masked_attn_offset_fwd", q, k, v, mask, scale, out, ())
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    out = _masked_call("masked_attn_offset_fwd", q, k, v, mask, scale, out, (), lse=lse)
+    return (out, lse) if return_lse else out
 
 
-def _masked_call(entry, q, k, v, mask, scale, out, extra):
+def _masked_call(entry, q, k, v, mask, scale, out, extra, lse=False):
     dev = q.device
     _check(q, "q", torch.bfloat16)
     _check(k, "k", torch.bfloat16, dev)
@@ -285,7 +289,8 @@ def _masked_call(entry, q, k, v, mask, scale, out, extra):
         out = torch.empty((B, Q, H, Dv), dtype=torch.bfloat16, device=dev)
     else:
         _check(out, "out", torch.bfloat16, dev)
-    _call(entry, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out), B, Q, KV, H, Dqk, Dv, padded_q, words,
+    lse_arg = () if lse is False else (_ptr(lse),)  # only the chunked-context entry takes lse
+    _call(entry, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out), *lse_arg, B, Q, KV, H, Dqk, Dv, padded_q, words,
           float(scale), *extra, _stream_ptr(dev))
     return out
 

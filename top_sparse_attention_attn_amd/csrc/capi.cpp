@@ -17,8 +17,9 @@ int sa_internal_launch_bitmask(const int32_t* idx, const int32_t* q_lens, const 
                                void* stream);
 int64_t sa_internal_bitmask_max_words(void);
 int sa_internal_launch_masked(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
-                              int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
-                              int64_t words, float scale, int mask_load_bits, int offset, void* stream);
+                              float* lse, int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv,
+                              int64_t padded_q, int64_t words, float scale, int mask_load_bits, int offset,
+                              void* stream);
 int sa_internal_candidate_gcols(int64_t rows, int64_t width);
 int sa_internal_launch_candidate_mask(float* logits, const int32_t* starts, const int32_t* ends, const uint8_t* flags,
                                       int64_t rows, int64_t width, int64_t stride_row, int64_t stride_col,
@@ -81,8 +82,8 @@ static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink
   return rc == 0 ? SA_OK : SA_ERR_HIP;
 }
 
-int masked_run(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, int64_t B, int64_t Q,
-               int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q, int64_t words, float scale,
+int masked_run(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, float* lse, int64_t B,
+               int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q, int64_t words, float scale,
                int mask_load_bits, int offset, void* stream) {
   if (B < 0 || Q < 0 || KV < 0 || H < 0 || Dqk < 0 || Dv < 0 || padded_q < 0 || words < 0) return SA_ERR_SHAPE;
   if (B * Q * H == 0) return SA_OK;
@@ -90,9 +91,10 @@ int masked_run(const void* q, const void* k, const void* v, const uint32_t* mask
   if (mask && (padded_q < Q || words % 4 != 0 || words > ((int64_t)1 << 22))) return SA_ERR_SHAPE;
   if (B * H * cdiv(Q, 128) > ((int64_t)1 << 31) - 1 || KV > ((int64_t)1 << 30)) return SA_ERR_SHAPE;
   if (!q || !out || (KV > 0 && (!k || !v))) return SA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || (k && !aligned16(k)) || (v && !aligned16(v)) || (mask && !aligned16(mask)))
+  if (!aligned16(q) || !aligned16(out) || (k && !aligned16(k)) || (v && !aligned16(v)) || (mask && !aligned16(mask)) ||
+      ((uintptr_t)lse & 3) != 0)
     return SA_ERR_ALIGN;
-  const int rc = sa_internal_launch_masked(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale,
+  const int rc = sa_internal_launch_masked(q, k, v, mask, out, lse, B, Q, KV, H, Dqk, Dv, padded_q, words, scale,
                                            mask_load_bits, offset, stream);
   return rc == 0 ? SA_OK : (rc == 2 ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
 }
@@ -189,16 +191,17 @@ int masked_attn_fwd(const void* q, const void* k, const void* v, const uint32_t*
                     float scale, int mask_load_bits, void* stream) {
   if (mask_load_bits != 128 && mask_load_bits != 32) return SA_ERR_SHAPE;
   if (mask && KV > 32 * words) return SA_ERR_SHAPE;
-  return masked_run(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale, mask_load_bits, 0, stream);
+  return masked_run(q, k, v, mask, out, nullptr, B, Q, KV, H, Dqk, Dv, padded_q, words, scale, mask_load_bits, 0,
+                    stream);
 }
 
-int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, int64_t B,
-                           int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
+int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, float* lse,
+                           int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
                            int64_t words, float scale, void* stream) {
   if (words < 0) return SA_ERR_SHAPE;
   if (B * Q * H > 0 && !mask) return SA_ERR_NULL;
   if (B * Q * H > 0 && words < 4) return SA_ERR_SHAPE;
-  return masked_run(q, k, v, mask, out, B, Q, KV, H, Dqk, Dv, padded_q, words, scale, 128, 1, stream);
+  return masked_run(q, k, v, mask, out, lse, B, Q, KV, H, Dqk, Dv, padded_q, words, scale, 128, 1, stream);
 }
 
 int candidate_mask_apply(float* logits, const int32_t* starts, const int32_t* ends, const uint8_t* flags,

@@ -16,6 +16,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // s_waitcnt with vmcnt = VM (0..63), lgkmcnt = 0, expcnt untouched.

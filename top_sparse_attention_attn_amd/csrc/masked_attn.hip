@@ -64,8 +64,8 @@ struct Smem {
 template <int DQK, int DV, int MASKBITS, bool OFFSET>
 __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const uint32_t* __restrict__ mask, __bf16* __restrict__ out, int Q, int KV, int H, int padded_q, int words,
-    int nxcc, float scale_log2) {
+    const uint32_t* __restrict__ mask, __bf16* __restrict__ out, float* __restrict__ lse, int Q, int KV, int H,
+    int padded_q, int words, int nxcc, float scale_log2) {
   using namespace masked;
   using SM = Smem<DQK, DV>;
   constexpr int KS = SM::KS, VS = SM::VS;
@@ -377,6 +377,10 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     const float L = c0 * sm.lsum[0][tid] + c1 * sm.lsum[1][tid];
     sm.fin[0][tid] = L > 0.f ? c0 / L : 0.f;
     sm.fin[1][tid] = L > 0.f ? c1 / L : 0.f;
+    // log-sum-exp of the query's scaled logits (natural log; -inf without any visible key):
+    // sum_j 2^(y_j) = L 2^M with y in log2 units
+    const int qo = qt * kQT + tid;
+    if (lse != nullptr && qo < Q) lse[((size_t)b * Q + qo) * H + h] = L > 0.f ? (M + __builtin_log2f(L)) * kLn2 : kNegInf;
   }
   wait_lgkm0();
   wg_barrier();  // factors ready; every wave is past its last tile, so the tile buffers are free
@@ -433,9 +437,9 @@ static int masked_device_xccs() {
 }  // namespace sa
 
 extern "C" int sa_internal_launch_masked(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
-                                         int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv,
-                                         int64_t padded_q, int64_t words, float scale, int mask_load_bits, int offset,
-                                         void* stream) {
+                                         float* lse, int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk,
+                                         int64_t Dv, int64_t padded_q, int64_t words, float scale, int mask_load_bits,
+                                         int offset, void* stream) {
   const int64_t nqt = (Q + sa::masked::kQT - 1) / sa::masked::kQT;
   const dim3 grid((unsigned)(B * H * nqt));
   const float sl2 = scale * sa::kLog2e;
@@ -443,7 +447,7 @@ extern "C" int sa_internal_launch_masked(const void* q, const void* k, const voi
   const int nxcc = sa::masked_device_xccs();
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(sa::masked::kThreads), 0, (hipStream_t)stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, mask, (__bf16*)out, (int)Q, (int)KV, (int)H, (int)padded_q,
+                       (const __bf16*)k, (const __bf16*)v, mask, (__bf16*)out, lse, (int)Q, (int)KV, (int)H, (int)padded_q,
                        (int)words, nxcc, sl2);
   };
   if (offset)
