@@ -227,7 +227,7 @@ def main():
             x = sets[i % nsets]
             sa.candidate_mask_apply(x["logits"], x["ends"], x["flags"], x["block_size"])
 
-        kernel_step, kernel_name = step, "candidate_mask_kernel<false>"
+        kernel_step, kernel_name = step, "candidate_mask_kernel<false, true>"
         work = [(candidate_work(x), 0.0, candidate_work(x)) for x in sets]
         units_per_step = cfg.rows
         unit = "decode rows/s"

@@ -133,3 +133,28 @@ def test_config_shape_sampled_rows(oracle_impl):
     ref = oracle_impl.candidate_mask(head.cpu().numpy(), e.cpu().numpy(), f_narrow.numpy(), inp["block_size"])
     _assert_contract(logits[:, :4096], head, ref, e.cpu().numpy())
     assert torch.equal(logits[:, 4096:4096 + 8192], tail)
+
+
+@pytest.mark.parametrize("block_size", [4, 16, 12])
+@pytest.mark.parametrize("misaligned", [False, True])
+def test_long_rows_both_store_forms(oracle_impl, block_size, misaligned):
+    """Long rows with ends anywhere in the row (not multiples of 4), starts of mixed alignment
+    (multiples of 4 take the 16-byte store form, the others the per-column form) and the edge
+    flag set on half the rows. misaligned: the rows start 4 bytes past a 16-byte boundary, so
+    the whole launch takes the per-column form. Every row is compared over its full width."""
+    width = 65536 + 12
+    ends = [width, width - 1, 3, 40001, 65535, 17, width - 2, 1027]
+    starts = [0, 8, -12, 4, 129, 3, 62, 1024]
+    g = torch.Generator().manual_seed(1000 + block_size + misaligned)
+    nb = -(-width // block_size)
+    flags = (torch.rand((len(ends), nb + 1), generator=g) < 0.5).to(torch.uint8)
+    flags[::2, -1] = 1
+    base = torch.randn((len(ends), width + 4), generator=g).to(DEV)
+    logits = base[:, 1:width + 1] if misaligned else base[:, :width]
+    e = torch.tensor(ends, dtype=torch.int32)
+    s = torch.tensor(starts, dtype=torch.int32)
+    before = logits.clone()
+    ref = _oracle(oracle_impl, before, e, s, flags, block_size)
+    sa.candidate_mask_apply(logits, e.to(DEV), flags.to(DEV), block_size, starts=s.to(DEV))
+    torch.cuda.synchronize()
+    _assert_contract(logits, before, ref, e.numpy())

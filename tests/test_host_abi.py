@@ -139,9 +139,9 @@ def test_candidate_mask_rejects_before_any_hip_call():
 
 
 def test_candidate_grid_depends_on_shapes_only():
-    assert sa.candidate_mask_grid(96, 1 << 20) == 96 * (2048 // 96)
+    assert sa.candidate_mask_grid(96, 1 << 20) == 96 * (4096 // 96)
     assert sa.candidate_mask_grid(1, 8192) == 8          # one workgroup per 1024-column tile at most
-    assert sa.candidate_mask_grid(4096, 1 << 20) == 4096  # at least one per row
+    assert sa.candidate_mask_grid(8192, 1 << 20) == 8192  # at least one per row
     assert sa.candidate_mask_grid(0, 100) == 0
 
 
