@@ -6,14 +6,17 @@
 // chunks; word words-1 of query row 0 holds the batch's key start when key starts are
 // stored.
 //
-// One workgroup builds one mask row in LDS (zeroed, then LDS atomic OR of every index of
-// the row), then writes the whole row, padding included, with 16-byte stores, so the
-// output needs no pre-zeroing. Rows past q_len and padded query rows are written as zeros.
+// One workgroup of two waves builds one mask row in LDS (zeroed, then LDS atomic OR of
+// every index of the row), then writes the whole row, padding included, with 16-byte
+// stores, so the output needs no pre-zeroing. Rows past q_len and padded query rows are
+// written as zeros. When topk is a multiple of 4 the indices come in with 16-byte loads,
+// all of a thread's loads in flight before its first atomic (small workgroups keep many
+// rows' loads in flight per CU).
 #include "common.h"
 
 namespace sa {
 
-constexpr int kMaskThreads = 256;
+constexpr int kMaskThreads = 128;
 constexpr int kMaskMaxWords = 32768;  // 128 KB of LDS per row
 
 __global__ __launch_bounds__(kMaskThreads) void topk_bitmask_kernel(const int* __restrict__ idx,
@@ -34,9 +37,30 @@ __global__ __launch_bounds__(kMaskThreads) void topk_bitmask_kernel(const int* _
   }
   if (qi < live) {
     const int* r = idx + ((size_t)b * Q + qi) * topk;
-    for (int k = t; k < topk; k += kMaskThreads) {
-      const int j = r[k];
-      if (j >= 0 && j < key_len) atomicOr(row_s + (j >> 5), 1u << (j & 31));
+    if ((topk & 3) == 0) {
+      // 16-byte index loads (rows start 16-byte aligned), up to eight per thread in flight
+      // before the first atomic
+      constexpr int kV = 8;
+      for (int k0 = 4 * t; k0 < topk; k0 += 4 * kMaskThreads * kV) {
+        int4 v[kV];
+#pragma unroll
+        for (int u = 0; u < kV; u++) {
+          const int k = k0 + u * 4 * kMaskThreads;
+          v[u] = k < topk ? *(const int4*)(r + k) : make_int4(-1, -1, -1, -1);
+        }
+#pragma unroll
+        for (int u = 0; u < kV; u++) {
+          const int jj[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (jj[e] >= 0 && jj[e] < key_len) atomicOr(row_s + (jj[e] >> 5), 1u << (jj[e] & 31));
+        }
+      }
+    } else {
+      for (int k = t; k < topk; k += kMaskThreads) {
+        const int j = r[k];
+        if (j >= 0 && j < key_len) atomicOr(row_s + (j >> 5), 1u << (j & 31));
+      }
     }
   }
   __syncthreads();
