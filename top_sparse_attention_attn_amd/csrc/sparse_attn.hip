@@ -164,7 +164,6 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   constexpr int QB = SCORE ? (HB > 4 ? 2 : 1) : 1;
   const int nq = SCORE ? ((sw + 4 < HB) ? 2 : ((sw < HB) ? 1 : 0)) : 0;
   bf16x8 qreg[QB][SCORE ? G::kDSteps : 1];
-  float l_fin[QB];
   if constexpr (SCORE) {
 #pragma unroll
     for (int qi = 0; qi < QB; qi++) {

@@ -94,7 +94,7 @@ def main(argv):
         "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <out>/copy_fetch -o p -- python3 bench.py --copy-calibration",
         "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <out>/copy_write -o p -- python3 bench.py --copy-calibration",
         f"python -m top_sparse_attention_attn_amd.profile_summary {config} <out>/trace <out>/fetch <out>/write "
-        f"<out>/copy_fetch <out>/copy_write {out_md}",
+        f"<out>/copy_fetch <out>/copy_write {os.path.relpath(out_md)}",
     ]
     sha = kernel_sources_sha256()
     lines = [f"# rocprofv3 summary: bench.py --config {config}", "",
