@@ -256,7 +256,7 @@ def main():
                 x = sets[i % nsets]
                 sa.masked_attn(x["q"], x["k"], x["v"], masks[i % nsets], x["scale"], out=out)
 
-            kernel_step, kernel_name = step, "masked_attn_kernel<192,128,128>"
+            kernel_step, kernel_name = step, "masked_attn_kernel<192,128,128,false,true>"
             work = [masked_work(x, masks[0].numel() * 4) for x in sets]
             work = [(w[0], w[1], w[0]) for w in work]
             units_per_step = cfg.B * cfg.Q

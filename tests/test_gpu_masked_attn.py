@@ -42,6 +42,26 @@ def test_small_topk_mask(oracle_impl, bits_):
     assert_close(to64(out), ref, f"masked small {bits_}")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.6])
+@pytest.mark.parametrize("offset", [False, True])
+def test_scale_signs(oracle_impl, scale, offset):
+    """A positive scale takes the kernel form that finds each query's maximum on the raw scores
+    and scales it once; zero and negative scales take the form that scales every score first.
+    Zero gives equal weights over the visible keys, a negative scale reverses the order of the
+    scores, and 0.6 makes the weights peaked. Both forms against the oracle, plain and chunked
+    (key start 0, where the chunked form reads the same bits)."""
+    inp, cfg, _ = _small(35, orc=oracle_impl)
+    inp = dict(inp, scale=scale)
+    mask = _oracle_mask(oracle_impl, inp["topk_idxs"], cfg.KV, key_starts=[0] * cfg.B)
+    if offset:
+        out = sa.masked_attn_offset(inp["q"], inp["k"], inp["v"], mask, scale)
+    else:
+        out = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, scale)
+    torch.cuda.synchronize()
+    ref = _ref(oracle_impl, inp, mask).reshape(cfg.B, cfg.Q, cfg.H, cfg.Dv)
+    assert_close(to64(out), ref, f"masked scale {scale} offset {offset}")
+
+
 def test_small_dense_and_null_mask(oracle_impl):
     inp, cfg, _ = _small(32, orc=oracle_impl)
     B, pq, W = sa.topk_bitmask_shape(cfg.B, cfg.Q, cfg.KV)

@@ -46,6 +46,22 @@ def test_shapes_and_splits(oracle_impl, D, H, splits):
     assert_close(to64(out).reshape(ref.shape), ref, f"D={D} H={H} splits={splits}")
 
 
+@pytest.mark.parametrize("K", [0, 1, 31, 33])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_few_slots(oracle_impl, K, splits):
+    """K = 0 (no slot: only the sink, so o = 0 exactly), one slot, a single ragged tile, one full
+    tile plus one slot; with the library's split choice and with three forced splits (more
+    splits than tiles for the small K)."""
+    inp = _custom(3, 2, 128, 512, 64, K, seed=40 + K, holes=0.05)
+    out = _run(inp, num_splits=splits)
+    torch.cuda.synchronize()
+    if K == 0:
+        assert torch.count_nonzero(out).item() == 0
+        return
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, f"K={K} splits={splits}")
+
+
 def test_all_invalid_is_exactly_zero():
     inp = _custom(2, 2, 128, 512, 100, 70, seed=3)
     inp["topk_idxs"].fill_(-1)

@@ -61,7 +61,10 @@ struct Smem {
 
 }  // namespace masked
 
-template <int DQK, int DV, int MASKBITS, bool OFFSET>
+// POS: the scale (scale_log2) is positive and finite. Then a query's tile maximum is taken over
+// the raw scores (masked to -inf) and scaled once, and each weight is exp2(fma(s, scale_log2, -m)):
+// no per-score multiply and subtract. Otherwise every score is scaled first.
+template <int DQK, int DV, int MASKBITS, bool OFFSET, bool POS>
 __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const uint32_t* __restrict__ mask, __bf16* __restrict__ out, float* __restrict__ lse, int Q, int KV, int H,
@@ -299,12 +302,16 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
       for (int jb = 0; jb < 2; jb++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const bool vis = (vg >> (16 * jb + i)) & 1u;
-          const float x = vis ? sacc[qb][jb][i] * scale_log2 : kNegInf;
+          // all ones if the key is visible, else zero: the score (raw if POS, else scaled) or -inf
+          // by one bit select
+          const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)vg, 16 * jb + i, 1);
+          const float sv = POS ? sacc[qb][jb][i] : sacc[qb][jb][i] * scale_log2;
+          const float x = __uint_as_float((sel & __float_as_uint(sv)) | (~sel & 0xff800000u));
           sacc[qb][jb][i] = x;
           tmax = __builtin_elementwise_maximum(tmax, x);
         }
       tmax = max4_x16_x32(tmax);
+      if constexpr (POS) tmax *= scale_log2;  // the maximum of the scaled scores
       const float mold = m_ref[qb];
       const bool move = tmax > mold + 8.0f;  // also true for the first finite maximum
       const float mnew = move ? tmax : mold;
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          pv[i] = exp2_fast(sacc[qb][hf][i] - msub);
+          pv[i] = exp2_fast(POS ? __builtin_fmaf(sacc[qb][hf][i], scale_log2, -msub) : sacc[qb][hf][i] - msub);
           lsum = (hf == 0 && i == 0) ? pv[0] : lsum + pv[i];
         }
         pk[2 * hf] = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
@@ -450,11 +457,16 @@ extern "C" int sa_internal_launch_masked(const void* q, const void* k, const voi
                        (const __bf16*)k, (const __bf16*)v, mask, (__bf16*)out, lse, (int)Q, (int)KV, (int)H, (int)padded_q,
                        (int)words, nxcc, sl2);
   };
-  if (offset)
-    launch(sa::masked_attn_kernel<192, 128, 128, true>);
-  else if (mask_load_bits == 32)
-    launch(sa::masked_attn_kernel<192, 128, 32, false>);
-  else
-    launch(sa::masked_attn_kernel<192, 128, 128, false>);
+  const bool pos = sl2 > 0.f && sl2 < __builtin_huge_valf();
+  if (offset) {
+    if (pos) launch(sa::masked_attn_kernel<192, 128, 128, true, true>);
+    else launch(sa::masked_attn_kernel<192, 128, 128, true, false>);
+  } else if (mask_load_bits == 32) {
+    if (pos) launch(sa::masked_attn_kernel<192, 128, 32, false, true>);
+    else launch(sa::masked_attn_kernel<192, 128, 32, false, false>);
+  } else {
+    if (pos) launch(sa::masked_attn_kernel<192, 128, 128, false, true>);
+    else launch(sa::masked_attn_kernel<192, 128, 128, false, false>);
+  }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
