@@ -578,8 +578,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 // partials). The block's partials are 16-byte chunks of the MFMA output layout
 // [d block][lane][4 heads]; every thread issues all its chunk loads of a group of up to four
 // splits before it waits, then the merged block is staged in LDS and stored row by row.
+// 512 threads (two chunks per thread at D = 512) measured faster than 128, 256 or 1024.
+constexpr int kCombineThreads = 512;
 template <int D, int HB>
-__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* __restrict__ ws_o,
+__global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(const __bf16* __restrict__ ws_o,
                                                                    const float* __restrict__ ws_lse,
                                                                    const float* __restrict__ sink,
                                                                    __bf16* __restrict__ out, int H, int nsplit,
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* 
   using G = Geo<D>;
   constexpr int HP = HB * 16;
   constexpr int kChunks = G::kNDB * 64 * 8 / 16;       // 16-byte chunks of one partial block
-  constexpr int kPerThread = (kChunks + 255) / 256;    // chunks per thread
+  constexpr int kPerThread = (kChunks + kCombineThreads - 1) / kCombineThreads;  // chunks per thread
   constexpr int kOutStride = D + 8;                    // bf16 per staged output row
   __shared__ float wgt[kMaxSplits * 16];
   __shared__ __attribute__((aligned(16))) __bf16 stage[16 * kOutStride];
@@ -619,7 +621,7 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* 
         const uint4* src = (const uint4*)(ws_o + ((size_t)(tok * nsplit + p0 + pp) * HP + hb * 16) * D);
 #pragma unroll
         for (int j = 0; j < kPerThread; j++) {
-          const int c = t + 256 * j;
+          const int c = t + kCombineThreads * j;
           if (c < kChunks) v[pp][j] = src[c];
         }
       }
@@ -649,7 +651,7 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* 
       if (pp < np) {
 #pragma unroll
         for (int j = 0; j < kPerThread; j++) {
-          const int c = t + 256 * j;
+          const int c = t + kCombineThreads * j;
           if (c >= kChunks) continue;
           const int hq = 4 * ((2 * (c & 31)) >> 4);
           const bf16x8 x = __builtin_bit_cast(bf16x8, v[pp][j]);
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* 
   // stage the merged 16 x D block as bf16 rows, then store each row with 16-byte writes
 #pragma unroll
   for (int j = 0; j < kPerThread; j++) {
-    const int c = t + 256 * j;
+    const int c = t + kCombineThreads * j;
     if (c >= kChunks) continue;
     const int lane0 = 2 * (c & 31), col = (c >> 5) * 16 + (lane0 & 15), hq = 4 * (lane0 >> 4);
 #pragma unroll
@@ -677,7 +679,7 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const __bf16* 
   }
   __syncthreads();
   constexpr int kRowChunks = D / 8;  // 16-byte chunks per output row
-  for (int c = t; c < 16 * kRowChunks; c += 256) {
+  for (int c = t; c < 16 * kRowChunks; c += kCombineThreads) {
     const int r = c / kRowChunks, k = c % kRowChunks;
     const int h = hb * 16 + r;
     if (h < H) *(uint4*)(out + ((size_t)tok * H + h) * D + 8 * k) = *(const uint4*)(&stage[r * kOutStride + 8 * k]);
@@ -730,7 +732,7 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
     if (e != hipSuccess) return e;
   }
   if (nsplit == 1 || !(phases & 2)) return hipSuccess;
-  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)(ntok * HB)), dim3(256), 0, stream, ws_o, ws_lse,
+  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)(ntok * HB)), dim3(kCombineThreads), 0, stream, ws_o, ws_lse,
                      sink, (__bf16*)out, (int)H, nsplit, nxcc);
   return hipGetLastError();
 }
