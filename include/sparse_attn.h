@@ -91,6 +91,8 @@ int sparse_attn_num_splits(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K
  *            unspecified. Calls that may run at the same time need separate
  *            workspaces.
  * Supported: D in {64, 512}; 1 <= H <= 128. q, kv, out 16-byte aligned.
+ * Sizes: B*S <= 2^30, T <= 2^31, K <= 2^30, and B*S times the split count
+ * below 2^31; larger sizes return SA_ERR_SHAPE.
  */
 int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
                     int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,

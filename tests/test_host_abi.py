@@ -65,6 +65,8 @@ def test_sparse_rejects_before_any_hip_call():
     # empty work is accepted without a launch
     assert _sparse(B=0) == 0
     assert _sparse(S=0, q=None, out=None) == 0
+    # 2^30 tokens in 16 splits: 2^34 (token, split) pairs do not fit the launch
+    assert _sparse(B=1 << 30, D=512, T=1 << 20, K=1024, splits=16) == 2
 
 
 def test_workspace_policy():

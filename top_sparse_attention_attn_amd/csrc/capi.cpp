@@ -72,6 +72,7 @@ static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink
   if (!aligned16(q) || !aligned16(out) || (!fp8 && kv && !aligned16(kv))) return SA_ERR_ALIGN;
   if (((uintptr_t)attn_sink & 3u) || (topk_idxs && ((uintptr_t)topk_idxs & 3u))) return SA_ERR_ALIGN;
   const int nsplit = choose_splits(B, S, K, num_splits);
+  if (B * S * nsplit > ((int64_t)1 << 31) - 1) return SA_ERR_SHAPE;  // (token, split) pairs are int
   const size_t need = sparse_ws_bytes(B, S, H, D, nsplit);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return SA_ERR_WORKSPACE;
