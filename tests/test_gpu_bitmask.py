@@ -64,6 +64,24 @@ def test_single_equals_batched():
     assert torch.equal(full[1:2], one)
 
 
+def test_index_list_4byte_aligned(oracle_impl):
+    """topk a multiple of 4 but the index list only 4-byte aligned (a view one int32 into a
+    buffer): the build reads it with 4-byte loads and gives the same bits as an aligned copy."""
+    B, Q, topk, key_len = 2, 100, 64, 3000
+    g = torch.Generator().manual_seed(77)
+    src = torch.randint(-1, key_len + 5, (B, Q, topk), generator=g, dtype=torch.int32)
+    buf = torch.zeros(B * Q * topk + 4, dtype=torch.int32, device=DEV)
+    view = buf[1:1 + B * Q * topk].view(B, Q, topk)
+    view.copy_(src.to(DEV))
+    assert view.data_ptr() % 16 == 4
+    got = sa.topk_bitmask_build(view, key_len)
+    aligned = sa.topk_bitmask_build(src.to(DEV).contiguous(), key_len)
+    torch.cuda.synchronize()
+    ref = oracle_impl.topk_mask_build(src.numpy(), key_len)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), ref)
+    assert torch.equal(got, aligned)
+
+
 def test_overwrites_garbage_and_stays_in_bounds():
     """The whole buffer is written (no pre-zeroing needed) and nothing outside it."""
     idx = torch.randint(0, 300, (2, 9, 20), dtype=torch.int32, device=DEV)

@@ -9,7 +9,8 @@
 // One workgroup of two waves builds one mask row in LDS (zeroed, then LDS atomic OR of
 // every index of the row), then writes the whole row, padding included, with 16-byte
 // stores, so the output needs no pre-zeroing. Rows past q_len and padded query rows are
-// written as zeros. When topk is a multiple of 4 the indices come in with 16-byte loads,
+// written as zeros. When topk is a multiple of 4 and the index list starts 16-byte aligned
+// (the interface asks for 4-byte alignment only), the indices come in with 16-byte loads,
 // all of a thread's loads in flight before its first atomic (small workgroups keep many
 // rows' loads in flight per CU).
 #include "common.h"
@@ -37,8 +38,8 @@ __global__ __launch_bounds__(kMaskThreads) void topk_bitmask_kernel(const int* _
   }
   if (qi < live) {
     const int* r = idx + ((size_t)b * Q + qi) * topk;
-    if ((topk & 3) == 0) {
-      // 16-byte index loads (rows start 16-byte aligned), up to eight per thread in flight
+    if ((topk & 3) == 0 && ((uintptr_t)idx & 15u) == 0) {
+      // 16-byte index loads (every row starts 16-byte aligned), up to eight per thread in flight
       // before the first atomic
       constexpr int kV = 8;
       for (int k0 = 4 * t; k0 < topk; k0 += 4 * kMaskThreads * kV) {
