@@ -62,6 +62,24 @@ def test_few_slots(oracle_impl, K, splits):
     assert_close(to64(out).reshape(ref.shape), ref, f"K={K} splits={splits}")
 
 
+@pytest.mark.parametrize("splits", [4, 10])
+def test_empty_splits_leave_no_trace(oracle_impl, splits):
+    """Tokens whose valid slots end early (0, 1, 33, ... of 320): the later slot ranges hold no
+    gathered row. The workspace is filled with NaN bytes first, so a merge that read a block no
+    slot range wrote would show in the output."""
+    B, S, H, D, T, K = 8, 1, 128, 512, 600, 320
+    inp = _custom(B, S, H, D, T, K, seed=91, holes=0.0)
+    for bb, n in enumerate([0, 1, 33, 100, 160, 250, 319, 320]):
+        inp["topk_idxs"][bb, :, n:] = -1
+    ws = sa.new_workspace(sa.sparse_attn_workspace_bytes(B, S, H, D, K, splits), DEV)
+    ws.fill_(0xFF)
+    out = _run(inp, num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, f"empty splits, {splits} splits")
+    assert torch.count_nonzero(out[0]).item() == 0
+
+
 def test_all_invalid_is_exactly_zero():
     inp = _custom(2, 2, 128, 512, 100, 70, seed=3)
     inp["topk_idxs"].fill_(-1)
