@@ -163,6 +163,24 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   // position 64 t + key_start (eight 4-byte loads) into sm.mw[t & 1][query][4]. Rows past
   // padded_q read nothing.
   const int q0 = qt * kQT;
+  // the mask copy's lane offsets, tile independent (waves 4-7; the chunked form copies two
+  // groups of 64 words per wave, i = pw and pw + 4)
+  uint32_t moff[2] = {0u, 0u};
+  if (wave >= 4) {
+    const int pw = wave - 4;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      if constexpr (OFFSET) {
+        const int d = 64 * (pw + 4 * u) + lane;
+        moff[u] = (uint32_t)((d >> 2) * words + (d & 3)) * 4u;
+      } else if constexpr (MASKBITS == 128) {
+        moff[u] = (uint32_t)((64 * pw + lane) * words * 4);
+      } else {
+        const int d = 64 * pw + lane;
+        moff[u] = (uint32_t)((d >> 1) * words * 4 + (d & 1) * 4);
+      }
+    }
+  }
   auto mask_copy = [&](int t) {
     if (mask == nullptr || wave < 4) return;
     const int pw = wave - 4;
@@ -170,18 +188,13 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
                                  (uint32_t)(min(kQT, padded_q - q0) * words * 4));
     if constexpr (OFFSET) {
       const uint32_t w0 = (64u * (uint32_t)t + ksc) >> 5;
-      for (int i = pw; i < 8; i += 4) {
-        const int d = 64 * i + lane, ql = d >> 2;
-        dma_lds4(mr, (uint32_t)(ql * words + (int)w0 + (d & 3)) * 4u, lds_addr(sm.mw[t & 1]) + 256 * i);
-      }
+#pragma unroll
+      for (int u = 0; u < 2; u++) dma_lds4(mr, moff[u] + w0 * 4u, lds_addr(sm.mw[t & 1]) + 256 * (pw + 4 * u));
     } else if constexpr (MASKBITS == 128) {
-      if ((t & 1) == 0 && pw < 2) {
-        const int ql = 64 * pw + lane;
-        dma_lds16(mr, (uint32_t)(ql * words * 4 + (t >> 1) * 16), lds_addr(sm.mw[(t >> 1) & 1]) + 1024 * pw);
-      }
+      if ((t & 1) == 0 && pw < 2)
+        dma_lds16(mr, moff[0] + (uint32_t)(t >> 1) * 16u, lds_addr(sm.mw[(t >> 1) & 1]) + 1024 * pw);
     } else {
-      const int d = 64 * pw + lane, ql = d >> 1;
-      dma_lds4(mr, (uint32_t)(ql * words * 4 + (2 * t + (d & 1)) * 4), lds_addr(sm.mw[t & 1]) + 256 * pw);
+      dma_lds4(mr, moff[0] + (uint32_t)t * 8u, lds_addr(sm.mw[t & 1]) + 256 * pw);
     }
   };
 
@@ -190,6 +203,14 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   // buffer's range and read nothing. Returns the loads issued.
   constexpr int LK = DQK * 2 / 128, LV = DV * 2 / 128;
   static_assert(DQK * 2 % 128 == 0 && DV * 2 % 128 == 0, "rows are whole 128-byte lines");
+  // the first prefetch load's lane offset, tile independent (waves 0 and 1)
+  uint32_t pf_off0 = kOob;
+  if (wave < 2) {
+    const int LR = wave == 0 ? LK : LV, nlines = kKT * LR;
+    const int rowb = wave == 0 ? H * DQK * 2 : H * DV * 2;
+    const int L = qt + nqt * lane;
+    pf_off0 = L < nlines ? (uint32_t)((L / LR) * rowb + (L % LR) * 128) : kOob;
+  }
   auto prefetch = [&](int t) -> int {
     if (wave >= 2) return 0;
     const int nv = min(KV - t * kKT, kKT);
@@ -199,7 +220,11 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
                                : buffer_rsrc(v + row0 * DV, (uint32_t)(((nv - 1) * H + 1) * DV * 2));
     const int rowb = wave == 0 ? H * DQK * 2 : H * DV * 2;
     int n = 0;
-    for (int j0 = 0; qt + nqt * j0 < nlines; j0 += 64, n++) {
+    if (qt < nlines) {
+      dma_lds4(rs, pf_off0, lds_addr(sm.sink[wave]));
+      n++;
+    }
+    for (int j0 = 64; qt + nqt * j0 < nlines; j0 += 64, n++) {  // small query counts only
       const int L = qt + nqt * (j0 + lane);
       const uint32_t off = L < nlines ? (uint32_t)((L / LR) * rowb + (L % LR) * 128) : kOob;
       dma_lds4(rs, off, lds_addr(sm.sink[wave]));
