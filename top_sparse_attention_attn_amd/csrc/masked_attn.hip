@@ -130,15 +130,20 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   // kOob for a padding chunk. The offsets do not depend on the tile: each wave computes its own
   // once and the tile only moves the buffer's base.
   constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 7) / 8, VM = (VCH + 7) / 8;
+  // Load n of K goes to wave (n + 6) % 8 and load n of V to wave (n + 2) % 8, so the loads past a
+  // multiple of 8 land on waves 6, 7 (K) and 2, 3 (V), not on waves 0 and 1, which also issue the
+  // L2 prefetch (or on 4 and 5, which copy the mask words): every wave waits for the slowest at
+  // the tile barrier.
+  const int wk = (wave + 2) & 7, wvv = (wave + 6) & 7;  // this wave's first K / V load
   uint32_t koffs[KM], voffs[VM];
 #pragma unroll
   for (int m = 0; m < KM; m++) {
-    const int c = 64 * (wave + 8 * m) + lane, r = c / KCH, col = c % KCH;
+    const int c = 64 * (wk + 8 * m) + lane, r = c / KCH, col = c % KCH;
     koffs[m] = col < KLANES ? (uint32_t)(r * H * DQK * 2 + col * 16) : kOob;
   }
 #pragma unroll
   for (int m = 0; m < VM; m++) {
-    const int c = 64 * (wave + 8 * m) + lane, r = c / VCH, col = c % VCH;
+    const int c = 64 * (wvv + 8 * m) + lane, r = c / VCH, col = c % VCH;
     voffs[m] = col < VLANES ? (uint32_t)(r * H * DV * 2 + col * 16) : kOob;
   }
   auto gather = [&](int t) {
@@ -150,10 +155,10 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     const uint32_t kd = lds_addr(sm.k[t & 1]), vd = lds_addr(sm.v[t & 1]);
 #pragma unroll
     for (int m = 0; m < KM; m++)
-      if (wave + 8 * m < KCH) dma_lds16(kr, koffs[m], kd + 1024 * (wave + 8 * m));
+      if (wk + 8 * m < KCH) dma_lds16(kr, koffs[m], kd + 1024 * (wk + 8 * m));
 #pragma unroll
     for (int m = 0; m < VM; m++)
-      if (wave + 8 * m < VCH) dma_lds16(vr, voffs[m], vd + 1024 * (wave + 8 * m));
+      if (wvv + 8 * m < VCH) dma_lds16(vr, voffs[m], vd + 1024 * (wvv + 8 * m));
   };
 
   // Mask copy for tile t, by waves 4-7 (pw = 0..3): the wide form copies the 4 words of keys
