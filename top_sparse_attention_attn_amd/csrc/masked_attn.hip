@@ -25,12 +25,10 @@
 // buffer loads that write LDS directly, the padded LDS tile filled as one contiguous byte range,
 // 64 lanes x 16 bytes per load: a lane whose 16 bytes fall in a row's padding, or in a row past
 // KV, gets an offset beyond the buffer's range, so the hardware reads nothing for it (44 loads
-// per tile). They are waited for only at the next tile's barrier.
-// The workgroups of one (batch, head) walk the same tiles at about the same time, so without
-// help each of them would wait for the first one's HBM misses on every tile: waves 0 and 1
-// therefore touch the tile kPrefetch tiles ahead (4 bytes per 128-byte line, each workgroup
-// a 1/nqt share of the lines) to bring it into L2 early. Those loads write a scratch LDS
-// word and are waited for only at the next barrier, so they never stall a wave.
+// per tile). They are waited for only at the next tile's barrier. Issuing such a load holds the
+// issuing wave, and every wave waits for the slowest at the tile barrier, so the loads (and the
+// mask-word copies) are spread to give no wave more than six per tile; an L2 prefetch of later
+// tiles cost more in issue than it saved.
 // The row strides (416 and 288 bytes) and the row order of the transposed reads were chosen
 // with the LDS bank-conflict counter. One barrier per tile.
 #include "common.h"
@@ -43,7 +41,6 @@ constexpr int kQT = 128;  // queries per workgroup
 constexpr int kKT = 64;   // keys per tile
 constexpr int kThreads = 512;
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset beyond every range used here
-constexpr int kPrefetch = 3;            // L2 prefetch distance in tiles
 
 template <int DQK, int DV>
 struct Smem {
@@ -52,7 +49,6 @@ struct Smem {
   unsigned char k[2][kKT * KS];            // K tiles t (in use), t+1 (being copied)
   unsigned char v[2][kKT * VS];            // V tiles t (in use), t+1 (being copied)
   uint32_t mw[2][kQT * 4];                 // mask words: [chunk parity][query][4], or [tile parity][query][2]
-  uint32_t sink[2][64];                    // destination of the L2 prefetch loads (never read)
   float alpha[8][2][16];                   // per wave: rescale factor per query of a moved reference
   float mref[2][kQT];                      // per key half: final reference maximum per query
   float lsum[2][kQT];                      // per key half: final weight sum per query
@@ -131,9 +127,8 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   // once and the tile only moves the buffer's base.
   constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 7) / 8, VM = (VCH + 7) / 8;
   // Load n of K goes to wave (n + 6) % 8 and load n of V to wave (n + 2) % 8, so the loads past a
-  // multiple of 8 land on waves 6, 7 (K) and 2, 3 (V), not on waves 0 and 1, which also issue the
-  // L2 prefetch (or on 4 and 5, which copy the mask words): every wave waits for the slowest at
-  // the tile barrier.
+  // multiple of 8 land on waves 6, 7 (K) and 2, 3 (V), not on waves 4 and 5, which copy the mask
+  // words: every wave waits for the slowest at the tile barrier.
   const int wk = (wave + 2) & 7, wvv = (wave + 6) & 7;  // this wave's first K / V load
   uint32_t koffs[KM], voffs[VM];
 #pragma unroll
@@ -203,40 +198,6 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     }
   };
 
-  // L2 prefetch of tile t by waves 0 (K) and 1 (V): 128-byte line L of the tile (row L / LR,
-  // part L % LR) is touched by the workgroup with qt = L % nqt. Rows past KV are out of the
-  // buffer's range and read nothing. Returns the loads issued.
-  constexpr int LK = DQK * 2 / 128, LV = DV * 2 / 128;
-  static_assert(DQK * 2 % 128 == 0 && DV * 2 % 128 == 0, "rows are whole 128-byte lines");
-  // the first prefetch load's lane offset, tile independent (waves 0 and 1)
-  uint32_t pf_off0 = kOob;
-  if (wave < 2) {
-    const int LR = wave == 0 ? LK : LV, nlines = kKT * LR;
-    const int rowb = wave == 0 ? H * DQK * 2 : H * DV * 2;
-    const int L = qt + nqt * lane;
-    pf_off0 = L < nlines ? (uint32_t)((L / LR) * rowb + (L % LR) * 128) : kOob;
-  }
-  auto prefetch = [&](int t) -> int {
-    if (wave >= 2) return 0;
-    const int nv = min(KV - t * kKT, kKT);
-    const size_t row0 = ((size_t)b * KV + (size_t)t * kKT) * H + h;
-    const int LR = wave == 0 ? LK : LV, nlines = kKT * LR;
-    const u32x4 rs = wave == 0 ? buffer_rsrc(k + row0 * DQK, (uint32_t)(((nv - 1) * H + 1) * DQK * 2))
-                               : buffer_rsrc(v + row0 * DV, (uint32_t)(((nv - 1) * H + 1) * DV * 2));
-    const int rowb = wave == 0 ? H * DQK * 2 : H * DV * 2;
-    int n = 0;
-    if (qt < nlines) {
-      dma_lds4(rs, pf_off0, lds_addr(sm.sink[wave]));
-      n++;
-    }
-    for (int j0 = 64; qt + nqt * j0 < nlines; j0 += 64, n++) {  // small query counts only
-      const int L = qt + nqt * (j0 + lane);
-      const uint32_t off = L < nlines ? (uint32_t)((L / LR) * rowb + (L % LR) * 128) : kOob;
-      dma_lds4(rs, off, lds_addr(sm.sink[wave]));
-    }
-    return n;
-  };
-
   // The tiles start zeroed: if a skipped (out-of-range) chunk leaves LDS untouched, the rows past
   // KV still hold finite values, which the zero weights of their masked keys then cancel.
   {
@@ -251,20 +212,14 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     gather(0);
     mask_copy(0);
   }
-  // prefetch loads issued after this wave's last tile copies: vector-memory loads complete in
-  // issue order, so the copies have landed once only these may still be outstanding
-  int pf_out = 0;
-  for (int t = 1; t < kPrefetch && t < nkt; t++) pf_out += prefetch(t);
-
   // The two waves of a SIMD (the key halves of one query quarter) would otherwise run each phase
   // (QK MFMAs, softmax VALU work, P V MFMAs) at the same time; the key-half-0 wave gets issue
   // priority, so it runs ahead and each wave's softmax lands beside the other's MFMAs.
   if (kh == 0) __builtin_amdgcn_s_setprio(2);
 
   for (int t = 0; t < nkt; t++) {
-    wait_vm_lgkm0_dyn(pf_out);  // this wave's copies of tile t have landed
-    wg_barrier();               // tile t visible; everyone is done with tile t-1's buffers
-    pf_out = 0;
+    wait_vm_lgkm0<0>();  // this wave's copies of tile t have landed
+    wg_barrier();        // tile t visible; everyone is done with tile t-1's buffers
     if (t + 1 < nkt) {
       gather(t + 1);
       mask_copy(t + 1);
@@ -391,7 +346,6 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
 #pragma unroll
       for (int qb = 0; qb < QB; qb++) oacc[qb][db] = mfma16x16x32(pop[qb], bv, oacc[qb][db]);
     }
-    if (t + kPrefetch < nkt) pf_out = prefetch(t + kPrefetch);
   }
 
   // ---- merge the two key halves and store. Every wave publishes each query's reference maximum
