@@ -121,10 +121,10 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     for (int db = 0; db < NDB; db++) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Tile copies, shared by all 8 waves: the K tile in LDS is KCH 16-byte chunks per row (KLANES
-  // of data, then padding), 64 rows: KCH loads of 64 chunks each; V likewise with VCH. Load n
-  // belongs to wave n % 8; a lane's byte offset is taken relative to row 0 of the tile (head h),
-  // kOob for a padding chunk. The offsets do not depend on the tile: each wave computes its own
-  // once and the tile only moves the buffer's base.
+  // of data, then padding), 64 rows: KCH loads of 64 chunks each; V likewise with VCH. Each load
+  // belongs to one wave (below); a lane's byte offset is taken relative to row 0 of the tile (head
+  // h), kOob for a padding chunk. The offsets do not depend on the tile: each wave computes its
+  // own once and the tile only moves the buffer's base.
   constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 7) / 8, VM = (VCH + 7) / 8;
   // Load n of K goes to wave (n + 6) % 8 and load n of V to wave (n + 2) % 8, so the loads past a
   // multiple of 8 land on waves 6, 7 (K) and 2, 3 (V), not on waves 4 and 5, which copy the mask
