@@ -131,7 +131,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
                                           const float* __restrict__ sink, const int* __restrict__ idx,
                                           __bf16* __restrict__ out, __bf16* __restrict__ ws_o,
                                           float* __restrict__ ws_lse, int S, int H, int T, int K, int nsplit,
-                                          int nxcc, float scale_log2) {
+                                          int nxcc, int tok_mul, float scale_log2) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
   constexpr int NB = SCORE ? 0 : G::kDBV;  // output column blocks of this wave
@@ -148,7 +148,12 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   const int db0 = SCORE ? 0 : sw * G::kDBV;
   const bool pv_active = !SCORE && db0 < G::kNDB;
 
-  const int pair = xcd_local_id(blockIdx.x, gridDim.x, nxcc);
+  int pair = xcd_local_id(blockIdx.x, gridDim.x, nxcc);
+  // One split per token: tokens in a scrambled order (pair * tok_mul mod the token count, tok_mul
+  // coprime with it), so each round of workgroups mixes tokens from the whole sequence (early
+  // tokens have fewer causally valid slots) and the rounds do not load queries and store outputs
+  // all at the same time.
+  if (nsplit == 1) pair = (int)(((long)pair * tok_mul) % (long)gridDim.x);
   const int tok = pair / nsplit, split = pair % nsplit;
   const int b = tok / S;
   const int ntiles_all = (K + kTile - 1) / kTile;
@@ -564,12 +569,14 @@ template <int D, int HB, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ sink,
     const int* __restrict__ idx, __bf16* __restrict__ out, __bf16* __restrict__ ws_o, float* __restrict__ ws_lse,
-    int S, int H, int T, int K, int nsplit, int nxcc, float scale_log2) {
+    int S, int H, int T, int K, int nsplit, int nxcc, int tok_mul, float scale_log2) {
   __shared__ __attribute__((aligned(16))) Smem<D, HB> sm;
   if (threadIdx.x < 256)  // waves 0-3
-    run_split<D, HB, true, F8>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, scale_log2);
+    run_split<D, HB, true, F8>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, tok_mul,
+                               scale_log2);
   else
-    run_split<D, HB, false, F8>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, scale_log2);
+    run_split<D, HB, false, F8>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, tok_mul,
+                                scale_log2);
 }
 
 // Merge the split partials of one (token, 16-head block) and add the sink once:
@@ -714,6 +721,15 @@ static int device_xccs() {
   return cache[dev];
 }
 
+// A multiplier near 0.618 n that is coprime with n (so pair -> pair * m mod n is a bijection).
+static int token_multiplier(int64_t n) {
+  if (n <= 2) return 1;
+  auto gcd = [](int64_t a, int64_t b) { while (b) { const int64_t t = a % b; a = b; b = t; } return a; };
+  for (int64_t m = (int64_t)(0.6180339887 * (double)n) | 1; m < n; m += 2)
+    if (gcd(m, n) == 1) return (int)m;
+  return 1;
+}
+
 template <int D, int HB, bool F8>
 static hipError_t launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
                                 int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int nsplit,
@@ -727,7 +743,7 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
   if (phases & 1) {
     hipLaunchKernelGGL((sparse_attn_kernel<D, HB, F8>), dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q,
                        kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H, (int)T, (int)K, nsplit,
-                       nxcc, scale * kLog2e);
+                       nxcc, token_multiplier(n), scale * kLog2e);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
