@@ -126,10 +126,11 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   // h), kOob for a padding chunk. The offsets do not depend on the tile: each wave computes its
   // own once and the tile only moves the buffer's base.
   constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 7) / 8, VM = (VCH + 7) / 8;
-  // Load n of K goes to wave (n + 6) % 8 and load n of V to wave (n + 2) % 8, so the loads past a
-  // multiple of 8 land on waves 6, 7 (K) and 2, 3 (V), not on waves 4 and 5, which copy the mask
-  // words: every wave waits for the slowest at the tile barrier.
-  const int wk = (wave + 2) & 7, wvv = (wave + 6) & 7;  // this wave's first K / V load
+  // Load n of K goes to wave (n + 2) % 8 and load n of V to wave n % 8, so the loads past a
+  // multiple of 8 land on waves 2, 3 (K) and 0, 1 (V), not on waves 4 and 5, which copy the mask
+  // words. Every wave waits for the slowest at the tile barrier, and waves w and w + 4 share a
+  // SIMD: no wave issues more than 6 loads per tile and no SIMD more than 12.
+  const int wk = (wave + 6) & 7, wvv = wave;  // this wave's first K / V load
   uint32_t koffs[KM], voffs[VM];
 #pragma unroll
   for (int m = 0; m < KM; m++) {
