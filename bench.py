@@ -165,6 +165,7 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    post_timing = None  # extra measurement of a config, after its timed steps
     if args.config in ("decode", "decode_fp8", "prefill", "ragged", "tiny"):
         fp8 = args.config == "decode_fp8"
         cfg = wl.SPARSE_CONFIGS["decode" if fp8 else args.config]
@@ -256,7 +257,7 @@ def main():
                 x = sets[i % nsets]
                 sa.masked_attn(x["q"], x["k"], x["v"], masks[i % nsets], x["scale"], out=out)
 
-            kernel_step, kernel_name = step, "masked_attn_kernel<192,128,128,false,true>"
+            kernel_step, kernel_name = step, "masked_attn_kernel<192,128,128,false,true,false>"
             work = [masked_work(x, masks[0].numel() * 4) for x in sets]
             work = [(w[0], w[1], w[0]) for w in work]
             units_per_step = cfg.B * cfg.Q
@@ -272,6 +273,38 @@ def main():
                 return (lambda: orc.masked_attn(qb, kb, vb, m, x["scale"], rows)), len(rows)
 
             sample_desc = "every 64th query row of one step"
+
+            def mask_overhead():
+                """Time per call without a mask and with the all-ones and top-k masks, read with 16-byte
+                (4-word) and 4-byte loads: the comparison the mask-load change is measured by. Each
+                form runs 2 x 100 calls after 50 untimed ones, interleaved; the faster pass counts."""
+                ones = torch.full_like(masks[0], -1)
+                forms = {"none": (None, 128), "ones_128": (ones, 128), "ones_32": (ones, 32),
+                         "topk_128": (masks, 128), "topk_32": (masks, 32)}
+                best = {}
+                for _ in range(2):
+                    for name, (m, bits) in forms.items():
+                        def call(i):
+                            x = sets[i % nsets]
+                            mm = m[i % nsets] if isinstance(m, list) else m
+                            sa.masked_attn(x["q"], x["k"], x["v"], mm, x["scale"], out=out, mask_load_bits=bits)
+                        for i in range(50):
+                            call(i)
+                        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        torch.cuda.synchronize()
+                        a.record(stream)
+                        for i in range(100):
+                            call(i)
+                        b_.record(stream)
+                        torch.cuda.synchronize()
+                        us = a.elapsed_time(b_) * 10.0  # ms per 100 calls -> us per call
+                        best[name] = min(best.get(name, us), us)
+                res = {"us_per_call": {k: round(v, 2) for k, v in best.items()}}
+                res["overhead_pct"] = {k: round(100.0 * (v / best["none"] - 1.0), 1) for k, v in best.items()
+                                       if k != "none"}
+                return res
+
+            post_timing = mask_overhead
         else:
             outm = torch.empty_like(masks[0])
 
@@ -351,6 +384,8 @@ def main():
     roof["alg_flops_per_launch"] = flops
     roof["call_frac"] = call_frac  # the whole call (every kernel of one step) against the same peak
 
+    extra = post_timing() if post_timing is not None else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, make_cpu, 0, unit, sample_desc)
@@ -373,6 +408,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if extra is not None:
+        rec["mask_overhead"] = extra
     print(json.dumps(rec), flush=True)
 
 

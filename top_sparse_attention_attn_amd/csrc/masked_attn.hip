@@ -60,7 +60,8 @@ struct Smem {
 // POS: the scale (scale_log2) is positive and finite. Then a query's tile maximum is taken over
 // the raw scores (masked to -inf) and scaled once, and each weight is exp2(fma(s, scale_log2, -m)):
 // no per-score multiply and subtract. Otherwise every score is scaled first.
-template <int DQK, int DV, int MASKBITS, bool OFFSET, bool POS>
+// DENSE: no mask (every key visible); the scores of a tile inside the keys need no select.
+template <int DQK, int DV, int MASKBITS, bool OFFSET, bool POS, bool DENSE>
 __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const uint32_t* __restrict__ mask, __bf16* __restrict__ out, float* __restrict__ lse, int Q, int KV, int H,
@@ -280,22 +281,35 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     // key 4g + i for i < 4, 16 + 4g + i - 4 for i >= 4), so P never goes through LDS
     bf16x8 pop[QB];
     bool any_resc = false;
+    // No mask and a tile inside the keys: every key of the tile is visible (queries past Q are
+    // never stored), so the scores need no select.
+    const bool all_vis = DENSE && nvalid >= 32;
 #pragma unroll
     for (int qb = 0; qb < QB; qb++) {
       const uint32_t vg = (mwd[qb] & kvm) >> (4 * g);
       float tmax = kNegInf;
+      if (all_vis) {
 #pragma unroll
-      for (int jb = 0; jb < 2; jb++)
+        for (int jb = 0; jb < 2; jb++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          // all ones if the key is visible, else zero: the score (raw if POS, else scaled) or -inf
-          // by one bit select
-          const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)vg, 16 * jb + i, 1);
-          const float sv = POS ? sacc[qb][jb][i] : sacc[qb][jb][i] * scale_log2;
-          const float x = __uint_as_float((sel & __float_as_uint(sv)) | (~sel & 0xff800000u));
-          sacc[qb][jb][i] = x;
-          tmax = __builtin_elementwise_maximum(tmax, x);
-        }
+          for (int i = 0; i < 4; i++) {
+            if constexpr (!POS) sacc[qb][jb][i] *= scale_log2;
+            tmax = __builtin_elementwise_maximum(tmax, sacc[qb][jb][i]);
+          }
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            // all ones if the key is visible, else zero: the score (raw if POS, else scaled) or
+            // -inf by one bit select
+            const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)vg, 16 * jb + i, 1);
+            const float sv = POS ? sacc[qb][jb][i] : sacc[qb][jb][i] * scale_log2;
+            const float x = __uint_as_float((sel & __float_as_uint(sv)) | (~sel & 0xff800000u));
+            sacc[qb][jb][i] = x;
+            tmax = __builtin_elementwise_maximum(tmax, x);
+          }
+      }
       tmax = max4_x16_x32(tmax);
       if constexpr (POS) tmax *= scale_log2;  // the maximum of the scaled scores
       const float mold = m_ref[qb];
@@ -444,14 +458,17 @@ extern "C" int sa_internal_launch_masked(const void* q, const void* k, const voi
   };
   const bool pos = sl2 > 0.f && sl2 < __builtin_huge_valf();
   if (offset) {
-    if (pos) launch(sa::masked_attn_kernel<192, 128, 128, true, true>);
-    else launch(sa::masked_attn_kernel<192, 128, 128, true, false>);
+    if (pos) launch(sa::masked_attn_kernel<192, 128, 128, true, true, false>);
+    else launch(sa::masked_attn_kernel<192, 128, 128, true, false, false>);
+  } else if (mask == nullptr) {
+    if (pos) launch(sa::masked_attn_kernel<192, 128, 128, false, true, true>);
+    else launch(sa::masked_attn_kernel<192, 128, 128, false, false, true>);
   } else if (mask_load_bits == 32) {
-    if (pos) launch(sa::masked_attn_kernel<192, 128, 32, false, true>);
-    else launch(sa::masked_attn_kernel<192, 128, 32, false, false>);
+    if (pos) launch(sa::masked_attn_kernel<192, 128, 32, false, true, false>);
+    else launch(sa::masked_attn_kernel<192, 128, 32, false, false, false>);
   } else {
-    if (pos) launch(sa::masked_attn_kernel<192, 128, 128, false, true>);
-    else launch(sa::masked_attn_kernel<192, 128, 128, false, false>);
+    if (pos) launch(sa::masked_attn_kernel<192, 128, 128, false, true, false>);
+    else launch(sa::masked_attn_kernel<192, 128, 128, false, false, false>);
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
