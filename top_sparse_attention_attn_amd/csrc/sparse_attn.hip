@@ -685,11 +685,16 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
     }
   }
   __syncthreads();
+  // The output is not read again by this call, so it is stored nontemporally (streamed past the
+  // caches): decode calls 0.7-2 % and FP8 decode calls 1.6 % faster. Marking the partial loads
+  // the same way made ragged decode calls 5 % slower.
   constexpr int kRowChunks = D / 8;  // 16-byte chunks per output row
   for (int c = t; c < 16 * kRowChunks; c += kCombineThreads) {
     const int r = c / kRowChunks, k = c % kRowChunks;
     const int h = hb * 16 + r;
-    if (h < H) *(uint4*)(out + ((size_t)tok * H + h) * D + 8 * k) = *(const uint4*)(&stage[r * kOutStride + 8 * k]);
+    if (h < H)
+      __builtin_nontemporal_store(*(const u32x4*)(&stage[r * kOutStride + 8 * k]),
+                                  (u32x4*)(out + ((size_t)tok * H + h) * D + 8 * k));
   }
 }
 
