@@ -60,7 +60,9 @@ const char* sa_status_string(int status);
 /*   no valid slot and sink -inf gives o = 0.                                  */
 /*   Arithmetic: bf16 products, fp32 accumulation, fp32 softmax; the softmax   */
 /*   weights are rounded to bf16 before the weighted row sum; o is rounded to  */
-/*   bf16 (nearest even).                                                      */
+/*   bf16 (nearest even). When a token's slots are split over workgroups, each */
+/*   split's unnormalised weighted row sum (its weights relative to its own    */
+/*   reference maximum) is rounded to bf16 once before the merge.             */
 /* ------------------------------------------------------------------------ */
 
 /*
@@ -101,15 +103,17 @@ int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const
 /*
  * The two phases of sparse_attn_fwd, for callers that schedule them apart (to
  * overlap the merge with other work) or time them: sparse_attn_split_fwd runs
- * the attention over each token's split slot ranges and leaves normalised
- * partial outputs and their log-sum-exps in the workspace; sparse_attn_merge_fwd
- * merges them into `out`, adding the sink once (the identity: the split at
- * log-sum-exp e_p weighs 2^(e_p - M) / (sum_p 2^(e_p - M) + 2^(sink log2 e - M))).
+ * the attention over each token's split slot ranges and leaves, per split,
+ * the unnormalised weighted row sum O_p (bf16), its reference maximum m_p
+ * (log2 units) and weight sum l_p in the workspace; sparse_attn_merge_fwd
+ * merges them into `out`, adding the sink once (the identity
+ * o = sum_p 2^(m_p - M) O_p / (sum_p 2^(m_p - M) l_p + 2^(sink log2 e - M)),
+ * M the largest exponent).
  * When the split count resolves to 1, sparse_attn_split_fwd writes `out` in full
  * and sparse_attn_merge_fwd does nothing. Both take exactly sparse_attn_fwd's
  * arguments and checks; call them in this order on one stream with the same
- * arguments and workspace. Combined merge identity: DeepSeek V4 source notes,
- * ch. 5, section 5.5 (FlashMLA's split combine with the sink).
+ * arguments and workspace. Merge identity: "DeepSeek V4 源码剖析", ch. 5,
+ * section 5.5 (FlashMLA's split combine with the sink).
  */
 int sparse_attn_split_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
                           int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale, int num_splits,

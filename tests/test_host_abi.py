@@ -74,9 +74,12 @@ def test_workspace_policy():
     assert sa.sparse_attn_num_splits(1, 4096, 128, 512, 1152) == 1
     assert sa.sparse_attn_num_splits(1, 4, 8, 64, 32) == 1
     assert sa.sparse_attn_workspace_bytes(1, 4096, 128, 512, 1152) == 0
-    w = sa.sparse_attn_workspace_bytes(64, 1, 128, 512, 1152)
-    assert w == 64 * 4 * 128 * 512 * 2 + 64 * 4 * 128 * 4   # bf16 partials + fp32 lse
-    assert sa.sparse_attn_workspace_bytes(64, 1, 128, 512, 1152, 2) == 64 * 2 * 128 * 512 * 2 + 64 * 2 * 128 * 4
+    def r256(x):
+        return (x + 255) // 256 * 256
+    for n in (4, 2):  # bf16 partials, fp32 (m, l) per head
+        want = 64 * n * 128 * 512 * 2 + 64 * n * 128 * 8
+        assert sa.sparse_attn_workspace_bytes(64, 1, 128, 512, 1152, n) == want
+    assert sa.sparse_attn_workspace_bytes(64, 1, 128, 512, 1152) == sa.sparse_attn_workspace_bytes(64, 1, 128, 512, 1152, 4)
 
 
 def _mask(idx=FAKE, ql=None, ks=None, m=FAKE, B=1, Q=4, topk=8, key_len=100, pq=128, W=4):

@@ -143,7 +143,7 @@ def _workspace(device: torch.device, nbytes: int, workspace: torch.Tensor | None
         return workspace, workspace.numel()
     key = (device, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
-    if ws is None or ws.numel() < nbytes:
+    if ws is None or ws.numel() < nbytes + 256:
         ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     off = (-ws.data_ptr()) % 256
@@ -289,6 +289,8 @@ def _masked_call(entry, q, k, v, mask, scale, out, extra, lse=False):
         out = torch.empty((B, Q, H, Dv), dtype=torch.bfloat16, device=dev)
     else:
         _check(out, "out", torch.bfloat16, dev)
+        if tuple(out.shape) != (B, Q, H, Dv):
+            raise ValueError(f"out must be [{B}, {Q}, {H}, {Dv}]")
     lse_arg = () if lse is False else (_ptr(lse),)  # only the chunked-context entry takes lse
     _call(entry, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out), *lse_arg, B, Q, KV, H, Dqk, Dv, padded_q, words,
           float(scale), *extra, _stream_ptr(dev))

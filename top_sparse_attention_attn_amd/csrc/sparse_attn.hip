@@ -73,7 +73,6 @@ struct Smem {
   float lsum[HB * 16];
   float alpha[2][HB * 16];
   float fin[HB * 16];
-  float lsef[HB * 16];  // log-sum-exp (log2 units) of this split's weights per head
   unsigned char vmb[kBufs][8];  // per value wave: validity of its 4 rows of the tile (one byte each)
   int flag[2][4];
 };
@@ -130,7 +129,7 @@ template <int D, int HB, bool SCORE, bool F8>
 __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restrict__ q, const void* __restrict__ kv,
                                           const float* __restrict__ sink, const int* __restrict__ idx,
                                           __bf16* __restrict__ out, __bf16* __restrict__ ws_o,
-                                          float* __restrict__ ws_lse, int S, int H, int T, int K, int nsplit,
+                                          float* __restrict__ ws_ml, int S, int H, int T, int K, int nsplit,
                                           int nxcc, int tok_mul, float scale_log2) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
@@ -358,11 +357,6 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-#ifdef SA_PHASE_BARRIER
-    // The value waves start PV only once the K reads of the scores are issued, so PV's LDS
-    // traffic and MFMAs overlap the softmax instead of competing with QK.
-    wg_barrier();
-#endif
     // ---- online softmax of tile tt (score waves)
     if constexpr (SCORE) {
       if (tt < ntl) {
@@ -467,9 +461,9 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   unsigned lne = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   asm volatile("" : "+v"(lne));
   const int lanee = (int)lne, ge = lanee >> 4, l16e = lanee & 15;
-  // Per-head output factor f (score waves own the heads): with no split the sink is folded
-  // in, o = O 2^(m-M) / (l 2^(m-M) + 2^(sink-M)); with splits each split keeps its own
-  // normalised output O / l (bf16) and lse = m + log2(l), merged afterwards with the sink.
+  // Per-head output factor f of the no-split path (score waves own the heads): the sink is
+  // folded in, o = O 2^(m-M) / (l 2^(m-M) + 2^(sink-M)). With splits, each split's unnormalised
+  // O and its (m, l) are merged with the sink afterwards.
   if constexpr (SCORE) {
 #pragma unroll
     for (int qi = 0; qi < QB; qi++) {
@@ -477,7 +471,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
       const int h = (sw + 4 * qi) * 16 + l16e;
       const float m = sm.mref[h];
       const float l = sm.lsum[h];
-      float f = 0.f, lse = kNegInf;
+      float f = 0.f;
       if (nsplit == 1) {
         if (h < H) {
           const float sk = sink[h];
@@ -495,14 +489,8 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
             }
           }
         }
-      } else if (m > kNegInf && l > 0.f) {
-        f = 1.f / l;
-        lse = m + __builtin_log2f(l);
       }
-      if (ge == 0) {
-        sm.fin[h] = f;
-        sm.lsef[h] = lse;
-      }
+      if (ge == 0) sm.fin[h] = f;
     }
   }
   wait_lgkm0();
@@ -510,29 +498,25 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 
   const int tid = threadIdx.x;
   if (nsplit > 1) {
-    // split partial: the normalised block in the MFMA layout [head block][d block][lane][4 heads]
-    // (8 bytes per lane, 512 contiguous bytes per wave store) straight from the accumulators,
-    // and the log-sum-exps; merged with the other splits of the token (and the sink) by
-    // sparse_attn_combine_kernel
+    // split partial for sparse_attn_combine_kernel: the unnormalised block O in the MFMA layout
+    // [head block][d block][lane][4 heads] (8 bytes per lane, 512 contiguous bytes per wave
+    // store) straight from the accumulators, and (m, l) per head
     if constexpr (NB > 0) {
       if (pv_active) {
         __bf16* const wpart = ws_o + (size_t)pair * HP * D;
 #pragma unroll
         for (int hb = 0; hb < HB; hb++) {
-          float f[4];
-#pragma unroll
-          for (int i = 0; i < 4; i++) f[i] = sm.fin[hb * 16 + 4 * ge + i];
 #pragma unroll
           for (int db = 0; db < NB; db++) {
             bf16x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; i++) v[i] = (__bf16)(oacc[hb][db][i] * f[i]);
+            for (int i = 0; i < 4; i++) v[i] = (__bf16)oacc[hb][db][i];
             *(bf16x4*)(wpart + ((hb * G::kNDB + db0 + db) * 64 + lanee) * 4) = v;
           }
         }
       }
     }
-    if (tid < HP) ws_lse[(size_t)pair * HP + tid] = sm.lsef[tid];
+    if (tid < HP) *(float2*)(ws_ml + ((size_t)pair * HP + tid) * 2) = make_float2(sm.mref[tid], sm.lsum[tid]);
     return;
   }
 
@@ -568,19 +552,21 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 template <int D, int HB, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ sink,
-    const int* __restrict__ idx, __bf16* __restrict__ out, __bf16* __restrict__ ws_o, float* __restrict__ ws_lse,
+    const int* __restrict__ idx, __bf16* __restrict__ out, __bf16* __restrict__ ws_o, float* __restrict__ ws_ml,
     int S, int H, int T, int K, int nsplit, int nxcc, int tok_mul, float scale_log2) {
   __shared__ __attribute__((aligned(16))) Smem<D, HB> sm;
   if (threadIdx.x < 256)  // waves 0-3
-    run_split<D, HB, true, F8>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, tok_mul,
+    run_split<D, HB, true, F8>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, nxcc, tok_mul,
                                scale_log2);
   else
-    run_split<D, HB, false, F8>(sm, q, kv, sink, idx, out, ws_o, ws_lse, S, H, T, K, nsplit, nxcc, tok_mul,
+    run_split<D, HB, false, F8>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, nxcc, tok_mul,
                                 scale_log2);
 }
 
 // Merge the split partials of one (token, 16-head block) and add the sink once:
-// o = sum_p 2^(lse_p - M) o_p / (sum_p 2^(lse_p - M) + 2^(sink - M)), M the largest term.
+// o = sum_p 2^(m_p - M) O_p / (sum_p 2^(m_p - M) l_p + 2^(sink - M)), M the largest term, where
+// split p left its unnormalised output O_p (bf16) and its reference maximum m_p (log2 units)
+// and weight sum l_p.
 // Grid: tokens x head blocks (mapped so a token's blocks run on the XCD that wrote its
 // partials). The block's partials are 16-byte chunks of the MFMA output layout
 // [d block][lane][4 heads]; every thread issues all its chunk loads of a group of up to four
@@ -589,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 constexpr int kCombineThreads = 512;
 template <int D, int HB>
 __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(const __bf16* __restrict__ ws_o,
-                                                                   const float* __restrict__ ws_lse,
+                                                                   const float* __restrict__ ws_ml,
                                                                    const float* __restrict__ sink,
                                                                    __bf16* __restrict__ out, int H, int nsplit,
                                                                    int nxcc) {
@@ -610,14 +596,19 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
 #pragma unroll
   for (int j = 0; j < kPerThread; j++) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weights: thread t < 16 owns head hb*16+t; its log-sum-exp values are loaded in one round
-  float lse[kMaxSplits];
+  // weights: thread t < 16 owns head hb*16+t; its (m, l) values are loaded in one round
+  float mp[kMaxSplits], lp[kMaxSplits];
   float sk = kNegInf;
   if (t < 16) {
     const int h = hb * 16 + t;
     sk = h < H ? sink[h] : kNegInf;
 #pragma unroll
-    for (int p = 0; p < kMaxSplits; p++) lse[p] = p < nsplit ? ws_lse[((size_t)tok * nsplit + p) * HP + h] : kNegInf;
+    for (int p = 0; p < kMaxSplits; p++) {
+      const float2 v = p < nsplit ? *(const float2*)(ws_ml + (((size_t)tok * nsplit + p) * HP + h) * 2)
+                                  : make_float2(kNegInf, 0.f);
+      mp[p] = v.x;
+      lp[p] = v.y;
+    }
   }
   for (int p0 = 0; p0 < nsplit; p0 += 4) {
     const int np = nsplit - p0 < 4 ? nsplit - p0 : 4;
@@ -638,14 +629,17 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
         const float s2 = sk * kLog2e;
         float M = s2;
 #pragma unroll
-        for (int p = 0; p < kMaxSplits; p++) M = fmaxf(M, lse[p]);
-        float L = (s2 > kNegInf && M > kNegInf) ? exp2_fast(s2 - M) : 0.f;
+        for (int p = 0; p < kMaxSplits; p++) M = fmaxf(M, mp[p]);
+        float c[kMaxSplits], L = (s2 > kNegInf && M > kNegInf) ? exp2_fast(s2 - M) : 0.f;
 #pragma unroll
-        for (int p = 0; p < kMaxSplits; p++) L += (lse[p] > kNegInf) ? exp2_fast(lse[p] - M) : 0.f;
+        for (int p = 0; p < kMaxSplits; p++) {
+          c[p] = (mp[p] > kNegInf && M > kNegInf) ? exp2_fast(mp[p] - M) : 0.f;
+          L += c[p] * lp[p];
+        }
 #pragma unroll
         for (int p = 0; p < kMaxSplits; p++) {
           if (p >= nsplit) break;
-          float w = (lse[p] > kNegInf && M > kNegInf) ? exp2_fast(lse[p] - M) / L : 0.f;
+          float w = L > 0.f ? c[p] / L : 0.f;
           if (__builtin_isnan(sk)) w = __builtin_nanf("");
           else if (sk == __builtin_huge_valf()) w = 0.f;
           wgt[p * 16 + t] = w;
@@ -698,18 +692,18 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
   }
 }
 
-// Workspace of a split call: bf16 partials [pair][HP*D], then fp32 log-sum-exps [pair][HP]
-// (256-byte aligned parts). Pure scratch: contents on entry do not matter.
+// Workspace of a split call: unnormalised bf16 partials [pair][HP*D] (MFMA layout), then fp32
+// (m, l) [pair][HP][2] (256-byte aligned parts). Pure scratch: contents on entry do not matter.
 struct WsLayout {
-  size_t lse, total;
+  size_t ml, total;
 };
 static inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 static WsLayout ws_layout(int64_t ntok, int64_t HB, int64_t D, int nsplit) {
   WsLayout w{};
   if (nsplit <= 1) return w;
   const size_t pairs = (size_t)ntok * nsplit, hp = (size_t)HB * 16;
-  w.lse = round256(pairs * hp * D * 2);
-  w.total = w.lse + round256(pairs * hp * 4);
+  w.ml = round256(pairs * hp * D * 2);
+  w.total = w.ml + round256(pairs * hp * 8);
   return w;
 }
 
@@ -743,17 +737,17 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
   const int64_t n = ntok * nsplit;
   const WsLayout L = ws_layout(ntok, HB, D, nsplit);
   __bf16* ws_o = nsplit > 1 ? (__bf16*)ws : nullptr;
-  float* ws_lse = nsplit > 1 ? (float*)((char*)ws + L.lse) : nullptr;
+  float* ws_ml = nsplit > 1 ? (float*)((char*)ws + L.ml) : nullptr;
   const int nxcc = device_xccs();
   if (phases & 1) {
     hipLaunchKernelGGL((sparse_attn_kernel<D, HB, F8>), dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q,
-                       kv, sink, idx, (__bf16*)out, ws_o, ws_lse, (int)S, (int)H, (int)T, (int)K, nsplit,
+                       kv, sink, idx, (__bf16*)out, ws_o, ws_ml, (int)S, (int)H, (int)T, (int)K, nsplit,
                        nxcc, token_multiplier(n), scale * kLog2e);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (nsplit == 1 || !(phases & 2)) return hipSuccess;
-  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)(ntok * HB)), dim3(kCombineThreads), 0, stream, ws_o, ws_lse,
+  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)(ntok * HB)), dim3(kCombineThreads), 0, stream, ws_o, ws_ml,
                      sink, (__bf16*)out, (int)H, nsplit, nxcc);
   return hipGetLastError();
 }
