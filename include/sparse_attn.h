@@ -93,7 +93,7 @@ int sparse_attn_num_splits(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K
  *            unspecified. Calls that may run at the same time need separate
  *            workspaces.
  * Supported: D in {64, 512}; 1 <= H <= 128. q, kv, out 16-byte aligned.
- * Sizes: B*S <= 2^30, T <= 2^31, K <= 2^30, and B*S times the split count
+ * Sizes: B*S <= 2^30, T < 2^31, K <= 2^30, and B*S times the split count
  * below 2^31; larger sizes return SA_ERR_SHAPE.
  */
 int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
@@ -168,7 +168,9 @@ int topk_bitmask_shape(int64_t B, int64_t max_q_len, int64_t max_key_len, int re
  *              some slot of topk_idxs[b][q] equals j with 0 <= j < key_len;
  *              mask[b][0][words-1] = key_starts[b] when key_starts is given;
  *              every other word is 0.
- * Requires padded_q >= Q, words % 4 == 0, 32 * words >= key_len, mask 16-byte aligned.
+ * Requires padded_q >= Q, words % 4 == 0, 32 * words >= key_len, mask 16-byte aligned;
+ * words <= 32768 (else SA_ERR_UNSUPPORTED); B * padded_q < 2^31, topk < 2^31 and
+ * B * Q * topk <= 2^40 (else SA_ERR_SHAPE).
  */
 int topk_bitmask_build(const int32_t* topk_idxs, const int32_t* q_lens, const int32_t* key_starts, uint32_t* mask,
                        int64_t B, int64_t Q, int64_t topk, int64_t key_len, int64_t padded_q, int64_t words,
@@ -194,8 +196,9 @@ int topk_bitmask_build(const int32_t* topk_idxs, const int32_t* q_lens, const in
  * mask_load_bits  128: the mask is read as aligned 16-byte chunks (4 words per
  *                 128 keys); 32: one 32-bit word per 32 keys (control variant).
  *                 Both give bitwise-identical outputs.
- * Supported: (Dqk, Dv) = (192, 128). Requires padded_q >= Q, words % 4 == 0,
- * words <= 2^22, 32 * words >= KV, KV <= 2^30; q, k, v, mask, out 16-byte aligned.
+ * Supported: (Dqk, Dv) = (192, 128), H <= 4096 (else SA_ERR_UNSUPPORTED).
+ * Requires padded_q >= Q, words % 4 == 0, words <= 2^21, 32 * words >= KV,
+ * KV <= 2^30, Q < 2^31 (else SA_ERR_SHAPE); q, k, v, mask, out 16-byte aligned.
  */
 int masked_attn_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out,
                     int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,
@@ -220,6 +223,7 @@ int masked_attn_fwd(const void* q, const void* k, const void* v, const uint32_t*
  *            vLLM PR #48770, review discussion). 4-byte aligned.
  * Requires mask != NULL (when B*Q*H > 0), words >= 4, words % 4 == 0,
  * padded_q >= Q; KV is not limited by words. Returns SA_ERR_NULL without a mask.
+ * The size limits of masked_attn_fwd apply (H <= 4096, words <= 2^21, ...).
  */
 int masked_attn_offset_fwd(const void* q, const void* k, const void* v, const uint32_t* mask, void* out, float* lse,
                            int64_t B, int64_t Q, int64_t KV, int64_t H, int64_t Dqk, int64_t Dv, int64_t padded_q,

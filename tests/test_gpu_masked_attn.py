@@ -129,6 +129,25 @@ def test_masked_config_sampled(oracle_impl):
     assert_close(got, ref, "masked config")
 
 
+def test_masked_config_no_mask_and_all_ones(oracle_impl):
+    """The masked config's shape (B=2, Q=2048, KV=8192, H=8) with no mask and with an all-ones
+    mask (the benchmark's mask-overhead forms): bitwise equal to each other (both 16- and 4-byte
+    mask loads), and sampled rows of every 128-query tile against the oracle's dense attention."""
+    inp = wl.masked_inputs("masked", 1006, DEV)
+    cfg = inp["config"]
+    mask = sa.topk_bitmask_build(inp["topk_idxs"], cfg.KV)
+    ones = torch.full_like(mask, -1)
+    none = sa.masked_attn(inp["q"], inp["k"], inp["v"], None, inp["scale"])
+    all1 = sa.masked_attn(inp["q"], inp["k"], inp["v"], ones, inp["scale"])
+    all1_32 = sa.masked_attn(inp["q"], inp["k"], inp["v"], ones, inp["scale"], mask_load_bits=32)
+    torch.cuda.synchronize()
+    assert torch.equal(none, all1) and torch.equal(all1, all1_32)
+    rows = np.concatenate([np.arange(b * cfg.Q + 37, (b + 1) * cfg.Q, 128) for b in range(cfg.B)] + [[0, cfg.Q - 1]])
+    ref = _ref(oracle_impl, inp, None, rows)
+    got = to64(none.reshape(cfg.B * cfg.Q, cfg.H, cfg.Dv)[torch.as_tensor(rows, device=DEV)])
+    assert_close(got, ref, "masked config, no mask")
+
+
 # --------------------------------------------------------------------------- chunked-context (offset) form
 def _chunk(inp, start, n, seed):
     """k, v of a chunk of n keys (fresh values: the chunk is any slice of a longer context)."""

@@ -69,6 +69,17 @@ def test_sparse_rejects_before_any_hip_call():
     assert _sparse(B=1 << 30, D=512, T=1 << 20, K=1024, splits=16) == 2
 
 
+def test_size_limits_before_any_hip_call():
+    # T = 2^31 would wrap to a negative int inside the kernel
+    assert _sparse(T=1 << 31) == 2
+    # topk beyond int32
+    assert _mask(topk=1 << 31, Q=1, B=1) == 2
+    # masked: too many heads for the kernel's 32-bit tile offsets; too many mask words
+    assert _masked(H=4097) == 4
+    assert _masked(W=(1 << 21) + 4, KV=64) == 2
+    assert _masked(Q=1 << 31, pq=1 << 31) == 2
+
+
 def test_workspace_policy():
     assert sa.sparse_attn_num_splits(64, 1, 128, 512, 1152) == 4
     assert sa.sparse_attn_num_splits(1, 4096, 128, 512, 1152) == 1

@@ -32,6 +32,12 @@ namespace {
 constexpr int kTileRows = 32;   // slot tile of the sparse kernel
 constexpr int kMaxSplits = 16;  // combine kernel limit
 constexpr int64_t kTargetWorkgroups = 256;  // one per CU on MI355X
+constexpr int64_t kInt32Max = ((int64_t)1 << 31) - 1;
+// Masked attention: the kernel's per-tile byte offsets are 32-bit; with at most kMaskedMaxHeads
+// heads and kMaskedMaxWords mask words they stay below 2^31 (64 key rows of H * 384 bytes; 256
+// mask rows of 4 * words bytes).
+constexpr int64_t kMaskedMaxHeads = 4096;
+constexpr int64_t kMaskedMaxWords = (int64_t)1 << 21;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -67,7 +73,7 @@ static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink
   if (fp8 && (D != 512 || T * 584 > ((int64_t)1 << 31) - 1)) return fp8 && D != 512 ? SA_ERR_UNSUPPORTED : SA_ERR_SHAPE;
   if (fp8 && kv && ((uintptr_t)kv & 7u)) return SA_ERR_ALIGN;
   if (H > 128) return SA_ERR_UNSUPPORTED;
-  if (B * S > (int64_t)1 << 30 || T > (int64_t)1 << 31 || K > (int64_t)1 << 30) return SA_ERR_SHAPE;
+  if (B * S > (int64_t)1 << 30 || T > kInt32Max || K > (int64_t)1 << 30) return SA_ERR_SHAPE;
   if (!q || !attn_sink || !out || (K > 0 && !topk_idxs) || (T > 0 && K > 0 && !kv)) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || (!fp8 && kv && !aligned16(kv))) return SA_ERR_ALIGN;
   if (((uintptr_t)attn_sink & 3u) || (topk_idxs && ((uintptr_t)topk_idxs & 3u))) return SA_ERR_ALIGN;
@@ -89,8 +95,10 @@ int masked_run(const void* q, const void* k, const void* v, const uint32_t* mask
   if (B < 0 || Q < 0 || KV < 0 || H < 0 || Dqk < 0 || Dv < 0 || padded_q < 0 || words < 0) return SA_ERR_SHAPE;
   if (B * Q * H == 0) return SA_OK;
   if (Dqk != 192 || Dv != 128) return SA_ERR_UNSUPPORTED;
-  if (mask && (padded_q < Q || words % 4 != 0 || words > ((int64_t)1 << 22))) return SA_ERR_SHAPE;
-  if (B * H * cdiv(Q, 128) > ((int64_t)1 << 31) - 1 || KV > ((int64_t)1 << 30)) return SA_ERR_SHAPE;
+  if (H > kMaskedMaxHeads) return SA_ERR_UNSUPPORTED;
+  if (mask && (padded_q < Q || words % 4 != 0 || words > kMaskedMaxWords)) return SA_ERR_SHAPE;
+  if (Q > kInt32Max || padded_q > kInt32Max || words > kMaskedMaxWords) return SA_ERR_SHAPE;
+  if (B * H * cdiv(Q, 128) > kInt32Max || KV > ((int64_t)1 << 30)) return SA_ERR_SHAPE;
   if (!q || !out || (KV > 0 && (!k || !v))) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || (k && !aligned16(k)) || (v && !aligned16(v)) || (mask && !aligned16(mask)) ||
       ((uintptr_t)lse & 3) != 0)
@@ -176,7 +184,7 @@ int topk_bitmask_build(const int32_t* topk_idxs, const int32_t* q_lens, const in
   if (key_starts && (words < cdiv(key_len, 32) + 1 || padded_q < 1)) return SA_ERR_SHAPE;
   if (B * padded_q == 0 || words == 0) return SA_OK;
   if (words > sa_internal_bitmask_max_words()) return SA_ERR_UNSUPPORTED;
-  if (B * padded_q > ((int64_t)1 << 31) - 1 || B * Q * topk > ((int64_t)1 << 40)) return SA_ERR_SHAPE;
+  if (B * padded_q > kInt32Max || topk > kInt32Max || B * Q * topk > ((int64_t)1 << 40)) return SA_ERR_SHAPE;
   if (!mask || (Q > 0 && topk > 0 && !topk_idxs)) return SA_ERR_NULL;
   if (!aligned16(mask)) return SA_ERR_ALIGN;
   if ((topk_idxs && ((uintptr_t)topk_idxs & 3u)) || (q_lens && ((uintptr_t)q_lens & 3u)) ||

@@ -789,3 +789,4 @@ extern "C" int sa_internal_launch_sparse(const void* q, const void* kv, const fl
 extern "C" size_t sa_internal_sparse_ws_bytes(int64_t ntok, int64_t H, int64_t D, int nsplit) {
   return sa::ws_layout(ntok, sa_internal_head_blocks(H), D, nsplit).total;
 }
+
