@@ -101,6 +101,24 @@ int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sparse_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same operation, arguments, checks and results as sparse_attn_fwd with
+ * num_splits resolved the same way, but without a workspace argument. The
+ * split partials live in a device array inside the library: 40 MiB per GPU,
+ * held from when the library is loaded until the process ends. A call whose
+ * sparse_attn_workspace_bytes(...) exceeds 40 MiB returns SA_ERR_WORKSPACE
+ * before any HIP call. Every call on one GPU shares that array, which keeps
+ * the last call's contents: calls that may overlap on one GPU (other streams
+ * or threads) race and give wrong results. The array's device address is
+ * looked up once per GPU, on that GPU's first call; the call allocates
+ * nothing.
+ */
+int sparse_attn_fwd_noalloc(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs,
+                            void* out, int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
+                            int num_splits, void* stream);
+
+/*
  * The two phases of sparse_attn_fwd, for callers that schedule them apart (to
  * overlap the merge with other work) or time them: sparse_attn_split_fwd runs
  * the attention over each token's split slot ranges and leaves, per split,

@@ -80,6 +80,16 @@ def test_size_limits_before_any_hip_call():
     assert _masked(Q=1 << 31, pq=1 << 31) == 2
 
 
+def test_noalloc_rejects_oversize_before_any_hip_call():
+    lib = _lib()
+    # 2048 tokens x 8 splits of 128 heads x 512: partials far beyond the 40 MiB scratch array
+    rc = lib.sparse_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 1, 128, 512, 4096, 1152, 0.1, 8, None)
+    assert rc == 5
+    # the ordinary argument checks come first
+    assert lib.sparse_attn_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 64, 16, 8, 0.1, 0, None) == 1
+    assert lib.sparse_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 100, 16, 8, 0.1, 0, None) == 4
+
+
 def test_workspace_policy():
     assert sa.sparse_attn_num_splits(64, 1, 128, 512, 1152) == 4
     assert sa.sparse_attn_num_splits(1, 4096, 128, 512, 1152) == 1

@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     sparse_attn,
     sparse_attn_fp8,
     sparse_attn_merge,
+    sparse_attn_noalloc,
     sparse_attn_split,
     sparse_attn_num_splits,
     sparse_attn_workspace_bytes,

@@ -22,6 +22,7 @@ SA_STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_ALIGN",
              5: "SA_ERR_WORKSPACE", 6: "SA_ERR_HIP"}
 
 EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_fwd",
+            "sparse_attn_fwd_noalloc",
             "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "sparse_attn_fp8_fwd", "topk_bitmask_shape", "topk_bitmask_build",
             "masked_attn_fwd", "masked_attn_offset_fwd", "candidate_mask_apply", "candidate_mask_grid"]
 
@@ -55,6 +56,8 @@ def _load():
         for name in ("sparse_attn_fwd", "sparse_attn_split_fwd", "sparse_attn_merge_fwd"):
             getattr(lib, name).argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
             getattr(lib, name).restype = I
+        lib.sparse_attn_fwd_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I, P]
+        lib.sparse_attn_fwd_noalloc.restype = I
         lib.sparse_attn_fp8_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
         lib.sparse_attn_fp8_fwd.restype = I
         lib.topk_bitmask_shape.argtypes = [I64, I64, I64, I, P]
@@ -163,6 +166,14 @@ def sparse_attn(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor, topk
     return _sparse_call("sparse_attn_fwd", q, kv, attn_sink, topk_idxs, scale, out, num_splits, workspace)
 
 
+def sparse_attn_noalloc(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor, topk_idxs: torch.Tensor,
+                        scale: float, out: torch.Tensor | None = None, num_splits: int = 0) -> torch.Tensor:
+    """sparse_attn through sparse_attn_fwd_noalloc: the split partials go to the library's own
+    40 MiB device array (shared by every call on the GPU), so no workspace is allocated. With
+    `out` given the call allocates nothing at all."""
+    return _sparse_call("sparse_attn_fwd_noalloc", q, kv, attn_sink, topk_idxs, scale, out, num_splits, None)
+
+
 def sparse_attn_split(q, kv, attn_sink, topk_idxs, scale, out=None, num_splits: int = 0, workspace=None):
     """First phase of sparse_attn (sparse_attn_split_fwd): split partials into `workspace`,
     or the full output when the call has one split. Pass the same workspace to sparse_attn_merge."""
@@ -204,6 +215,10 @@ def _sparse_call(entry, q, kv, attn_sink, topk_idxs, scale, out, num_splits, wor
         _check(out, "out", torch.bfloat16, dev)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
+    if entry == "sparse_attn_fwd_noalloc":
+        _call(entry, _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, S, H, D, T, K,
+              float(scale), int(num_splits), _stream_ptr(dev))
+        return out
     need = sparse_attn_workspace_bytes(B, S, H, D, K, num_splits)
     ws, ws_bytes = _workspace(dev, need, workspace)
     if fp8:

@@ -12,6 +12,8 @@ int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, 
                               int nsplit, void* ws, int phases, int fp8, void* stream);
 int sa_internal_head_blocks(int64_t H);
 size_t sa_internal_sparse_ws_bytes(int64_t ntok, int64_t H, int64_t D, int nsplit);
+size_t sa_internal_scratch_bytes(void);
+int sa_internal_scratch_ptr(void** out);
 int sa_internal_launch_bitmask(const int32_t* idx, const int32_t* q_lens, const int32_t* key_starts, uint32_t* mask,
                                int64_t B, int64_t Q, int64_t topk, int64_t key_len, int64_t padded_q, int64_t words,
                                void* stream);
@@ -63,10 +65,11 @@ size_t sparse_ws_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int nsplit) {
   return sa_internal_sparse_ws_bytes(B * S, H, D, nsplit);
 }
 
+// noalloc: take the workspace from the library's scratch array instead of the arguments
 static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,
                            int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
                            int num_splits, void* workspace, size_t workspace_bytes, void* stream, int phases,
-                           int fp8 = 0) {
+                           int fp8 = 0, int noalloc = 0) {
   if (!sparse_sizes_ok(B, S, H, D, K) || T < 0 || num_splits < 0 || num_splits > 64) return SA_ERR_SHAPE;
   if (B * S == 0 || H == 0) return SA_OK;
   if (D != 64 && D != 512) return SA_ERR_UNSUPPORTED;
@@ -80,7 +83,11 @@ static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink
   const int nsplit = choose_splits(B, S, K, num_splits);
   if (B * S * nsplit > ((int64_t)1 << 31) - 1) return SA_ERR_SHAPE;  // (token, split) pairs are int
   const size_t need = sparse_ws_bytes(B, S, H, D, nsplit);
-  if (need > 0) {
+  if (noalloc) {
+    if (need > sa_internal_scratch_bytes()) return SA_ERR_WORKSPACE;
+    workspace = nullptr;
+    if (need > 0 && sa_internal_scratch_ptr(&workspace) != 0) return SA_ERR_HIP;
+  } else if (need > 0) {
     if (!workspace || workspace_bytes < need) return SA_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255u) return SA_ERR_ALIGN;
   }
@@ -141,6 +148,13 @@ int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const
                     void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_attn_run(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, num_splits, workspace,
                          workspace_bytes, stream, 3);
+}
+
+int sparse_attn_fwd_noalloc(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs,
+                            void* out, int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
+                            int num_splits, void* stream) {
+  return sparse_attn_run(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, num_splits, nullptr, 0, stream, 3,
+                         0, 1);
 }
 
 int sparse_attn_split_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,

@@ -33,6 +33,8 @@
 //    so the scores and P V run unchanged on bf16 rows while HBM moves 584 bytes per row.
 #include <stddef.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace sa {
@@ -790,3 +792,29 @@ extern "C" size_t sa_internal_sparse_ws_bytes(int64_t ntok, int64_t H, int64_t D
   return sa::ws_layout(ntok, sa_internal_head_blocks(H), D, nsplit).total;
 }
 
+// ---- Scratch of the allocation-free entry point (sparse_attn_fwd_noalloc): the split partials of
+// one call live in this file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only stands in for the
+// symbol): each device's address is looked up once, with that device current, and cached.
+namespace {
+constexpr size_t kScratchBytes = (size_t)40 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+}  // namespace
+
+extern "C" size_t sa_internal_scratch_bytes(void) { return kScratchBytes; }
+
+// Device address of the current device's scratch array (0 on success).
+extern "C" int sa_internal_scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return 1;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
