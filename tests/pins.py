@@ -54,24 +54,23 @@ def _run_sparse(o, q, kv, sink, idx, scale):
 
 
 def pages_loop(q, kv, sink, idx, scale):
-    """The pages' loop semantics ("DeepSeek V4 源码剖析" section 5.2) in float64 torch:
-    gather the K rows (an index of -1 gathers the last row, as python indexing does),
-    mask invalid logits to -inf, append the sink logit, softmax, and sum the gathered
-    rows with the first K weights (the sink's weight is dropped)."""
+    """The semantics that "DeepSeek V4 源码剖析" section 5.2 states for sparse_attn, written out
+    independently of the oracle as one batched float64 computation: for every token and head
+    the logits of the gathered rows are scale * q.k; a slot is empty when its index is negative
+    (it gets no weight); with M the largest of the token's valid logits and the head's sink, each
+    valid slot weighs exp(x - M) and the sink adds exp(sink - M) to the denominator only."""
     B, S, H, D = q.shape
-    K = idx.shape[-1]
-    out = torch.zeros(B, S, H, D, dtype=torch.float64)
-    for b in range(B):
-        for s in range(S):
-            for h in range(H):
-                gathered = _f64(kv[b, idx[b, s].long()])
-                valid = idx[b, s] >= 0
-                logits = (_f64(q[b, s, h]) @ gathered.T) * scale
-                logits = torch.where(valid, logits, torch.tensor(float("-inf"), dtype=torch.float64))
-                with_sink = torch.cat([logits, sink[h:h + 1].to(torch.float64)])
-                weights = torch.softmax(with_sink, dim=0)
-                out[b, s, h] = (weights[:K, None] * gathered).sum(dim=0)
-    return out.numpy()
+    qf = _f64(q)                                             # [B,S,H,D]
+    valid = idx >= 0                                         # [B,S,K]
+    safe = idx.clamp(min=0).long()
+    rows = torch.stack([_f64(kv[b])[safe[b]] for b in range(B)])   # [B,S,K,D]
+    logits = torch.einsum("bshd,bskd->bshk", qf, rows) * scale      # [B,S,H,K]
+    logits = logits.masked_fill(~valid[:, :, None, :], float("-inf"))
+    sk = _f64(sink).view(1, 1, H, 1)
+    top = torch.maximum(logits.amax(dim=-1, keepdim=True), sk)      # [B,S,H,1]
+    w = torch.exp(logits - top)                                     # empty slots: exp(-inf) = 0
+    denom = w.sum(dim=-1, keepdim=True) + torch.exp(sk - top)
+    return (torch.einsum("bshk,bskd->bshd", w, rows) / denom).numpy()
 
 
 def sdpa_with_sink(qv, keys, sink_value, scale):
@@ -88,8 +87,8 @@ def sdpa_with_sink(qv, keys, sink_value, scale):
 
 # --------------------------------------------------------------------------- sparse_attn pins
 def check_loop_semantics(o):
-    """The oracle equals the pages' loop (section 5.2) on tiny inputs, with and without
-    duplicate slots."""
+    """The oracle equals the stated semantics of section 5.2 (pages_loop) on tiny inputs, with
+    and without duplicate slots."""
     q, kv, sink, idx = _tiny(seed=1)
     scale = 16 ** -0.5
     got = _run_sparse(o, q, kv, sink, idx, scale).reshape(q.shape)
