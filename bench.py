@@ -126,24 +126,52 @@ def candidate_work(inp) -> float:
     return float(total)
 
 
-def cpu_baseline(args, make_call_inputs, unit_per_call: float, unit: str, sample_desc: str):
-    """Time the CPU oracle (as it stands) on the host cores for a bounded sample."""
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    import oracle
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    orc = oracle.Oracle()
-    fn, units = make_call_inputs(orc)
+
+def cpu_baseline(args, orc, fn, units: float, unit: str, sample_desc: str):
+    """Time the CPU oracle (as it stands) on the host cores for a bounded sample: on all the
+    threads OpenMP gives it, then on one thread."""
     fn()  # first call outside the clock (page-in)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        fn()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or el > 30.0:
-            break
-    return {"value": units * n / el, "unit": unit, "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"{sample_desc}, repeated {n} times in {el:.1f} s"}
+
+    def rate(seconds: float):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or el > 30.0:
+                return units * n / el, n, el
+
+    cores = orc.num_threads()
+    v, n, el = rate(args.cpu_seconds)
+    orc.set_num_threads(1)
+    v1, n1, el1 = rate(min(args.cpu_seconds / 2.0, 5.0))
+    orc.set_num_threads(cores)
+    return {"value": v, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{sample_desc}, repeated {n} times in {el:.1f} s",
+            "value_1core": v1, "sample_1core": f"repeated {n1} times in {el1:.1f} s on 1 thread",
+            "cpu_model": cpu_model()}
+
+
+def max_error(got, ref) -> dict:
+    """Max abs error of GPU values against the oracle's, and the fraction within the parity
+    tolerance |gpu - ref| <= 2e-2 + 2e-2 |ref| (NaN where the oracle has NaN counts as equal)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    both_nan = np.isnan(got) & np.isnan(ref)
+    err = np.where(both_nan, 0.0, np.abs(got - ref))
+    ok = both_nan | (err <= 2e-2 + 2e-2 * np.abs(ref))
+    return {"max_abs_err": float(np.nanmax(err)) if err.size else 0.0,
+            "within_tolerance": float(ok.mean()) if ok.size else 1.0, "compared": int(ok.size)}
 
 
 def main():
@@ -206,17 +234,23 @@ def main():
         extra_cfg = {"B": cfg.B, "S": cfg.S, "H": cfg.H, "D": cfg.D, "T": cfg.T, "K": cfg.K,
                      "num_splits": sa.sparse_attn_num_splits(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)}
 
+        ntok = cfg.B * cfg.S
+        toks = np.arange(ntok) if args.config != "prefill" else np.arange(0, ntok, 64)
+
         def make_cpu(orc):
             x = sets[0]
             qb = oracle_bits(x["q"])
             sk, ix = x["attn_sink"].cpu().numpy(), x["topk_idxs"].cpu().numpy()
-            ntok = cfg.B * cfg.S
-            toks = np.arange(ntok) if args.config != "prefill" else np.arange(0, ntok, 64)
             if fp8:
                 kv8 = x["kv"].cpu().numpy()
                 return (lambda: orc.sparse_attn_fp8(qb, kv8, sk, ix, x["scale"], toks)), len(toks)
             kvb = oracle_bits(x["kv"])
             return (lambda: orc.sparse_attn(qb, kvb, sk, ix, x["scale"], toks)), len(toks)
+
+        def gpu_sample():  # the same tokens of input set 0, from a fresh call
+            step(0)
+            torch.cuda.synchronize()
+            return out.reshape(ntok, cfg.H, cfg.D)[torch.as_tensor(toks, device=dev)].float().cpu().numpy()
 
         sample_desc = ("all tokens of one step" if args.config != "prefill" else "every 64th token of one step")
     elif args.config in ("candidate", "candidate_long"):
@@ -238,11 +272,26 @@ def main():
         extra_cfg = {"rows": cfg.rows, "width": cfg.width, "block_size": cfg.block_size,
                      "grid": sa.candidate_mask_grid(cfg.rows, cfg.width)}
 
+        pristine = sets[0]["logits"].cpu().numpy().copy()  # set 0 before any step masks it
+
         def make_cpu(orc):
             x = sets[0]
-            lg = x["logits"].cpu().numpy()
             en, fl = x["ends"].cpu().numpy(), x["flags"].cpu().numpy()
-            return (lambda: orc.candidate_mask(lg, en, fl, cfg.block_size)), cfg.rows
+            return (lambda: orc.candidate_mask(pristine, en, fl, cfg.block_size)), cfg.rows
+
+        def gpu_sample():  # set 0's logits as the steps left them (the mask is idempotent)
+            torch.cuda.synchronize()
+            return sets[0]["logits"].cpu().numpy()
+
+        def candidate_error(got, ref):
+            """Columns below each row's end must equal the whole-row rule; columns at or past it
+            must be untouched."""
+            ends = sets[0]["ends"].cpu().numpy().astype(np.int64)
+            cols = np.arange(cfg.width)[None, :]
+            live = cols < np.minimum(ends, cfg.width)[:, None]
+            want = np.where(live, ref, pristine)
+            return {"mismatches": int((~((got == want) | (np.isnan(got) & np.isnan(want)))).sum()),
+                    "compared": int(got.size)}
 
         sample_desc = "all rows of one step, whole-row rule over the full width"
     else:
@@ -265,12 +314,18 @@ def main():
             bound = "mfma"
             workload = f"masked_attn B={cfg.B} Q={cfg.Q} KV={cfg.KV} H={cfg.H} qk=192 v=128, top-k mask 25% dense"
 
+            rows = np.arange(0, cfg.B * cfg.Q, 64)
+
             def make_cpu(orc):
                 x = sets[0]
                 qb, kb, vb = oracle_bits(x["q"]), oracle_bits(x["k"]), oracle_bits(x["v"])
                 m = orc.topk_mask_build(x["topk_idxs"].cpu().numpy(), cfg.KV)
-                rows = np.arange(0, cfg.B * cfg.Q, 64)
                 return (lambda: orc.masked_attn(qb, kb, vb, m, x["scale"], rows)), len(rows)
+
+            def gpu_sample():
+                step(0)
+                torch.cuda.synchronize()
+                return out.reshape(cfg.B * cfg.Q, cfg.H, cfg.Dv)[torch.as_tensor(rows, device=dev)].float().cpu().numpy()
 
             sample_desc = "every 64th query row of one step"
 
@@ -324,6 +379,14 @@ def main():
                 ix = sets[0]["topk_idxs"].cpu().numpy()
                 return (lambda: orc.topk_mask_build(ix, cfg.KV)), cfg.B * cfg.Q
 
+            def gpu_sample():
+                step(0)
+                torch.cuda.synchronize()
+                return outm.cpu().numpy().view(np.uint32)
+
+            def bitmask_error(got, ref):
+                return {"mismatched_words": int((got != ref).sum()), "compared": int(got.size)}
+
             sample_desc = "one full step"
         extra_cfg = {"B": cfg.B, "Q": cfg.Q, "KV": cfg.KV, "H": cfg.H}
 
@@ -364,6 +427,24 @@ def main():
     torch.cuda.synchronize()
     kms = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
 
+    # Per-call distribution (an event pair around every call, every launch queued ahead of the
+    # GPU) and a warm figure (input set 0 back to back, so its rows stay in the Infinity Cache).
+    torch.cuda.synchronize()
+    cpairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda._sleep(int(2.4e6 * max(1.0, 0.02 * args.steps)))
+    for i in range(args.steps):
+        cpairs[i][0].record(stream)
+        step(i)
+        cpairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in cpairs]))
+    e0.record(stream)
+    for i in range(args.steps):
+        step(0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) / args.steps * 1e3
+
     nbytes = sum(w[0] for w in work) / len(work)
     flops = sum(w[1] for w in work) / len(work)
     kbytes = sum(w[2] for w in work) / len(work)
@@ -386,9 +467,26 @@ def main():
 
     extra = post_timing() if post_timing is not None else None
 
+    # Accuracy on the timed inputs (set 0), outside the timed region: the oracle's output for
+    # the CPU baseline's sample against the GPU's for the same sample.
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import oracle
+
+    orc = oracle.Oracle()
+    fn, units = make_cpu(orc)
+    got = gpu_sample()
+    ref = fn()
+    if args.config in ("candidate", "candidate_long"):
+        accuracy = candidate_error(got, ref)
+    elif args.config == "bitmask":
+        accuracy = bitmask_error(got, ref)
+    else:
+        accuracy = max_error(got.reshape(ref.shape), ref)
+    accuracy["sample"] = sample_desc + " of input set 0"
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, make_cpu, 0, unit, sample_desc)
+        cpu = cpu_baseline(args, orc, fn, units, unit, sample_desc)
 
     rec = {
         "metric": METRIC if args.config == "decode" else f"{args.config}: {unit}",
@@ -407,6 +505,11 @@ def main():
         "config": {"workload": workload, **extra_cfg},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "per_call_us": {"median": float(np.median(per_call)), "p10": float(np.percentile(per_call, 10)),
+                        "p90": float(np.percentile(per_call, 90)), "calls": int(per_call.size),
+                        "note": "one event pair per call, rotating input sets"},
+        "warm_us_per_call": warm_us,
+        "accuracy": accuracy,
     }
     if extra is not None:
         rec["mask_overhead"] = extra

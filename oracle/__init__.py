@@ -75,6 +75,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_candidate_mask.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     return lib
 
 
@@ -102,6 +104,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """OpenMP threads for later calls (timing on fewer cores)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     def sparse_attn(self, q_bits, kv_bits, sink, idx, scale, tokens=None) -> np.ndarray:
         """o[t, h, :] for the flat tokens t = b*S + s listed in ``tokens`` (all when None).

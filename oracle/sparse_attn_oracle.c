@@ -466,3 +466,13 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads later calls use (for timing on fewer cores; no effect
+   without OpenMP). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
