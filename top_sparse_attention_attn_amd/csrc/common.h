@@ -54,6 +54,11 @@ __device__ __forceinline__ void dma_lds16(u32x4 rs, uint32_t off, uint32_t m0add
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m0addr), "v"(off), "s"(rs) : "memory", "m0");
 }
+// The same with the nontemporal (streaming) hint, for data read once.
+__device__ __forceinline__ void dma_lds16_nt(u32x4 rs, uint32_t off, uint32_t m0addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(m0addr), "v"(off), "s"(rs) : "memory", "m0");
+}
 __device__ __forceinline__ void dma_lds4(u32x4 rs, uint32_t off, uint32_t m0addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(m0addr), "v"(off), "s"(rs) : "memory", "m0");

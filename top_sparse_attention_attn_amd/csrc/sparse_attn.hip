@@ -127,7 +127,7 @@ __device__ __forceinline__ void pv_step(Smem<D, HB>& sm, f32x4 (&oacc)[HB][NB > 
   }
 }
 
-template <int D, int HB, bool SCORE, bool F8>
+template <int D, int HB, bool SCORE, bool F8, bool NT>
 __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restrict__ q, const void* __restrict__ kv,
                                           const float* __restrict__ sink, const int* __restrict__ idx,
                                           __bf16* __restrict__ out, __bf16* __restrict__ ws_o,
@@ -224,15 +224,21 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
           n += 2;
           const uint32_t base = (uint32_t)row * kF8Row;
           const uint32_t ldst = lds_addr(dst);
-          if (lane < 36) dma_lds16(kv8rs, base + 16u * lane, ldst);
+          if (lane < 36) {
+            if constexpr (NT) dma_lds16_nt(kv8rs, base + 16u * lane, ldst);
+            else dma_lds16(kv8rs, base + 16u * lane, ldst);
+          }
           if (lane < 2) dma_lds4(kv8rs, base + 576u + 4u * lane, ldst + 576u);
         }
       } else if (row >= 0 && row < T) {
         vbits |= 1u << r;
         n++;
+        // NT (one token per batch, decode): a row serves one token only, so it is streamed (nt) and
+        // does not push the queries and the split partials out of L2. Otherwise neighbouring tokens
+        // share rows through L2.
         if (lane < G::kLanesPerRow)
           __builtin_amdgcn_global_load_lds((const void*)(kv_b + (size_t)row * D + lane * 8), (lds_void_t*)dst, 16, 0,
-                                           0);
+                                           NT ? 2 : 0);
       } else if (lane < G::kLanesPerRow) {
         *(uint4*)(dst + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
       }
@@ -551,17 +557,17 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   }
 }
 
-template <int D, int HB, bool F8>
+template <int D, int HB, bool F8, bool NT>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ sink,
     const int* __restrict__ idx, __bf16* __restrict__ out, __bf16* __restrict__ ws_o, float* __restrict__ ws_ml,
     int S, int H, int T, int K, int nsplit, int nxcc, int tok_mul, float scale_log2) {
   __shared__ __attribute__((aligned(16))) Smem<D, HB> sm;
   if (threadIdx.x < 256)  // waves 0-3
-    run_split<D, HB, true, F8>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, nxcc, tok_mul,
+    run_split<D, HB, true, F8, NT>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, nxcc, tok_mul,
                                scale_log2);
   else
-    run_split<D, HB, false, F8>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, nxcc, tok_mul,
+    run_split<D, HB, false, F8, NT>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, nxcc, tok_mul,
                                 scale_log2);
 }
 
@@ -742,9 +748,11 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
   float* ws_ml = nsplit > 1 ? (float*)((char*)ws + L.ml) : nullptr;
   const int nxcc = device_xccs();
   if (phases & 1) {
-    hipLaunchKernelGGL((sparse_attn_kernel<D, HB, F8>), dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q,
-                       kv, sink, idx, (__bf16*)out, ws_o, ws_ml, (int)S, (int)H, (int)T, (int)K, nsplit,
-                       nxcc, token_multiplier(n), scale * kLog2e);
+    // one token per batch: the gathered rows are streamed (see run_split)
+    auto kern = S == 1 ? sparse_attn_kernel<D, HB, F8, true> : sparse_attn_kernel<D, HB, F8, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q, kv, sink, idx,
+                       (__bf16*)out, ws_o, ws_ml, (int)S, (int)H, (int)T, (int)K, nsplit, nxcc, token_multiplier(n),
+                       scale * kLog2e);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
