@@ -250,27 +250,24 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   // FP8: expand this wave's 4 rows of tile tt in place from the copied bytes to bf16 rows
   // (lanes 0-55: 8 e4m3 values of dims 8l .. 8l+7 with their tile's scale; lanes 56-63: 8 RoPE
   // dims), invalid rows to zeros. All reads land before any write: the bf16 row overlaps the
-  // bytes it is made from. Called once the tile's copies have landed (this wave's own rows).
+  // bytes it is made from. Branch-free across lanes: every lane reads 16 bytes and its tile's
+  // scale byte and converts; the RoPE lanes keep the raw bytes. Called once the tile's copies
+  // have landed (this wave's own rows).
   auto expand = [&](int tt) {
     const int bi = tt % kBufs;
     const unsigned vbits = __builtin_amdgcn_readfirstlane((unsigned)sm.vmb[bi][sw]);
-    uint2 f8[4];
-    uint4 rp[4];
+    const bool nope = lane < 56;
+    const int roff = nope ? 8 * lane : kF8Nope + 16 * (lane - 56);         // source bytes in the slot
+    const int woff = nope ? 16 * lane : 2 * kF8Nope + 16 * (lane - 56);    // bf16 destination
+    const int soff = 576 + (nope ? (lane >> 3) : 0);                       // scale byte
+    uint2 lo[4], hi[4];
     unsigned sb[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const unsigned char* slot = &sm.kv[bi][(sw * 4 + r) * G::kRowStride];
-      f8[r] = make_uint2(0u, 0u);
-      rp[r] = make_uint4(0u, 0u, 0u, 0u);
-      sb[r] = 0u;
-      if (vbits & (1u << r)) {
-        if (lane < 56) {
-          f8[r] = *(const uint2*)(slot + 8 * lane);
-          sb[r] = slot[576 + (lane >> 3)];
-        } else {
-          rp[r] = *(const uint4*)(slot + kF8Nope + 16 * (lane - 56));
-        }
-      }
+      lo[r] = *(const uint2*)(slot + roff);
+      hi[r] = *(const uint2*)(slot + roff + 8);
+      sb[r] = slot[soff];
     }
     wait_lgkm0();
     asm volatile("" ::: "memory");
@@ -278,22 +275,21 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     for (int r = 0; r < 4; r++) {
       unsigned char* slot = &sm.kv[bi][(sw * 4 + r) * G::kRowStride];
       uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (vbits & (1u << r)) {
-        if (lane < 56) {
-          // 2^(s-127) as an fp32 bit pattern (s = 0: the subnormal 2^-127; s = 255: NaN)
-          const unsigned bits = sb[r] == 0u ? 0x00400000u : (sb[r] == 255u ? 0x7fc00000u : sb[r] << 23);
-          const float sc = __uint_as_float(bits);
-          const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8[r].x, sc, false);
-          const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8[r].x, sc, true);
-          const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8[r].y, sc, false);
-          const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8[r].y, sc, true);
-          const bf16x8 v = bf16x8{a[0], a[1], c[0], c[1], d[0], d[1], e[0], e[1]};
-          w = *(const uint4*)&v;
-        } else {
-          w = rp[r];
-        }
+      if (vbits & (1u << r)) {  // wave-uniform
+        // 2^(s-127) as an fp32 bit pattern, in plain integer steps (no branches): s = 0 gives the
+        // subnormal 2^-127 (0x00400000 is the larger of the two), s = 255 sets the quiet bit of
+        // the infinity pattern (NaN)
+        const unsigned bits = __builtin_elementwise_max(sb[r] << 23, 0x00400000u) | (((sb[r] + 1u) >> 8) << 22);
+        const float sc = __uint_as_float(bits);
+        const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo[r].x, sc, false);
+        const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo[r].x, sc, true);
+        const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo[r].y, sc, false);
+        const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo[r].y, sc, true);
+        const bf16x8 v = bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+        const uint4 cv = __builtin_bit_cast(uint4, v);
+        w = nope ? cv : make_uint4(lo[r].x, lo[r].y, hi[r].x, hi[r].y);
       }
-      *(uint4*)(slot + (lane < 56 ? 16 * lane : 2 * kF8Nope + 16 * (lane - 56))) = w;
+      *(uint4*)(slot + woff) = w;
     }
   };
 
@@ -450,7 +446,11 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
         // iteration's copies are outstanding
         if (tt + 1 < ntl) {
           wait_vm_lgkm0_dyn(dma_new);
+          // the expansion is on this wave's path to the next barrier: it outranks the score
+          // waves' softmax for issue while it runs
+          __builtin_amdgcn_s_setprio(3);
           expand(tt + 1);
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       if (tt >= 1 && pv_active) {
