@@ -170,7 +170,46 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   constexpr int QB = SCORE ? (HB > 4 ? 2 : 1) : 1;
   const int nq = SCORE ? ((sw + 4 < HB) ? 2 : ((sw < HB) ? 1 : 0)) : 0;
   bf16x8 qreg[QB][SCORE ? G::kDSteps : 1];
-  if constexpr (SCORE) {
+  if constexpr (NT) {
+    // One token per batch (decode): every wave copies whole query rows (1 KB per wave instruction
+    // at D = 512) into the row ring, then the score waves read their B operands from there. Loaded
+    // straight into the operand layout (16 rows x 64 bytes per wave instruction) they landed 4.2 us
+    // after the workgroup's start at the decode shape; as whole rows, 2.6 us (operands included),
+    // although the row copies then start only once the queries are out of the ring.
+    static_assert(HP * G::kRowStride <= (int)sizeof(sm.kv), "queries exceed the ring");
+    for (int r = wave; r < HP; r += kThreads / 64) {
+      unsigned char* dst = &sm.kv[0][0] + r * G::kRowStride;
+      if (r < H) {
+        if (lane < G::kLanesPerRow)
+          __builtin_amdgcn_global_load_lds((const void*)(q + ((size_t)tok * H + r) * D + lane * 8), (lds_void_t*)dst, 16,
+                                           0, 0);
+      } else if (lane < G::kLanesPerRow) {
+        *(uint4*)(dst + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    wait_vm_lgkm0<0>();
+    wg_barrier();
+    if constexpr (SCORE) {
+#pragma unroll
+      for (int qi = 0; qi < QB; qi++) {
+        const int hr = (sw + 4 * qi) * 16 + l16;
+#pragma unroll
+        for (int s = 0; s < G::kDSteps; s++) {
+          bf16x8 v = {};
+          if (qi < nq) v = *(const bf16x8*)(&sm.kv[0][0] + hr * G::kRowStride + 64 * s + 16 * g);
+          qreg[qi][s] = v;
+        }
+        if (g == 0 && qi < nq) {
+          sm.mref[(sw + 4 * qi) * 16 + l16] = kNegInf;
+          sm.lsum[(sw + 4 * qi) * 16 + l16] = 0.f;
+        }
+      }
+      wait_lgkm0();
+    }
+    wg_barrier();  // the ring is free again for the row gather
+  } else if constexpr (SCORE) {
+    // Several tokens per batch (prefill): the queries go straight into the operand layout, beside
+    // the first row copies (staging them in the ring delays those copies: prefill 1.4 % slower).
 #pragma unroll
     for (int qi = 0; qi < QB; qi++) {
       const int h = (sw + 4 * qi) * 16 + l16;
