@@ -26,9 +26,10 @@
 // 64 lanes x 16 bytes per load: a lane whose 16 bytes fall in a row's padding, or in a row past
 // KV, gets an offset beyond the buffer's range, so the hardware reads nothing for it (44 loads
 // per tile). They are waited for only at the next tile's barrier. Issuing such a load holds the
-// issuing wave, and every wave waits for the slowest at the tile barrier, so the loads (and the
-// mask-word copies) are spread to give no wave more than six per tile; an L2 prefetch of later
-// tiles cost more in issue than it saved.
+// issuing wave, so the key-half-1 waves issue the K copies (and the mask words) while the
+// key-half-0 wave of each SIMD starts its MFMAs, and issues the V copies after them: the two waves
+// of a SIMD then run out of phase.
+// An L2 prefetch of later tiles cost more in issue than it saved.
 // The row strides (416 and 288 bytes) and the row order of the transposed reads were chosen
 // with the LDS bank-conflict counter. One barrier per tile.
 #include "common.h"
@@ -126,24 +127,27 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   // belongs to one wave (below); a lane's byte offset is taken relative to row 0 of the tile (head
   // h), kOob for a padding chunk. The offsets do not depend on the tile: each wave computes its
   // own once and the tile only moves the buffer's base.
-  constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 7) / 8, VM = (VCH + 7) / 8;
-  // Load n of K goes to wave (n + 2) % 8 and load n of V to wave n % 8, so the loads past a
-  // multiple of 8 land on waves 2, 3 (K) and 0, 1 (V), not on waves 4 and 5, which copy the mask
-  // words. Every wave waits for the slowest at the tile barrier, and waves w and w + 4 share a
-  // SIMD: no wave issues more than 6 loads per tile and no SIMD more than 12.
-  const int wk = (wave + 6) & 7, wvv = wave;  // this wave's first K / V load
+  constexpr int KCH = KS / 16, VCH = VS / 16, KM = (KCH + 3) / 4, VM = (VCH + 3) / 4;
+  // The key-half-1 waves (4-7) issue the K copies and the mask words right after the barrier (load n
+  // of K on wave 4 + n % 4); the key-half-0 waves, which have issue priority, start their MFMAs at
+  // once and issue the V copies after their QK (load n of V on wave n % 4). Issuing an LDS-DMA load
+  // holds the issuing wave, so the two waves of a SIMD then run out of phase. Measured per call:
+  // copies spread over all 8 waves at the barrier (at most 6 per wave) 3 % slower, all copies on
+  // key half 1 at the barrier 0.8 % slower, K on one half and V on the other both at the barrier
+  // 2 % slower, the V copies after key half 0's softmax 1 % slower.
+  const int wk = wave & 3, wvv = wave & 3;  // this wave's first K / V load
   uint32_t koffs[KM], voffs[VM];
 #pragma unroll
   for (int m = 0; m < KM; m++) {
-    const int c = 64 * (wk + 8 * m) + lane, r = c / KCH, col = c % KCH;
+    const int c = 64 * (wk + 4 * m) + lane, r = c / KCH, col = c % KCH;
     koffs[m] = col < KLANES ? (uint32_t)(r * H * DQK * 2 + col * 16) : kOob;
   }
 #pragma unroll
   for (int m = 0; m < VM; m++) {
-    const int c = 64 * (wvv + 8 * m) + lane, r = c / VCH, col = c % VCH;
+    const int c = 64 * (wvv + 4 * m) + lane, r = c / VCH, col = c % VCH;
     voffs[m] = col < VLANES ? (uint32_t)(r * H * DV * 2 + col * 16) : kOob;
   }
-  auto gather = [&](int t) {
+  auto gather = [&](int t, int part) {
     // rows t*kKT + r with r < nv are in range; the range ends inside row nv's first byte
     const int nv = min(KV - t * kKT, kKT);
     const size_t row0 = ((size_t)b * KV + (size_t)t * kKT) * H + h;
@@ -152,10 +156,10 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     const uint32_t kd = lds_addr(sm.k[t & 1]), vd = lds_addr(sm.v[t & 1]);
 #pragma unroll
     for (int m = 0; m < KM; m++)
-      if (wk + 8 * m < KCH) dma_lds16(kr, koffs[m], kd + 1024 * (wk + 8 * m));
+      if (part == 0 && wk + 4 * m < KCH) dma_lds16(kr, koffs[m], kd + 1024 * (wk + 4 * m));
 #pragma unroll
     for (int m = 0; m < VM; m++)
-      if (wvv + 8 * m < VCH) dma_lds16(vr, voffs[m], vd + 1024 * (wvv + 8 * m));
+      if (part == 1 && wvv + 4 * m < VCH) dma_lds16(vr, voffs[m], vd + 1024 * (wvv + 4 * m));
   };
 
   // Mask copy for tile t, by waves 4-7 (pw = 0..3): the wide form copies the 4 words of keys
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
   wait_lgkm0();
   wg_barrier();
   if (nkt > 0) {
-    gather(0);
+    gather(0, kh == 1 ? 0 : 1);  // K by key half 1, V by key half 0
     mask_copy(0);
   }
   // The two waves of a SIMD (the key halves of one query quarter) would otherwise run each phase
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
     wait_vm_lgkm0<0>();  // this wave's copies of tile t have landed
     wg_barrier();        // tile t visible; everyone is done with tile t-1's buffers
     if (t + 1 < nkt) {
-      gather(t + 1);
+      if (kh == 1) gather(t + 1, 0);
       mask_copy(t + 1);
     }
     const int par = t & 1;
@@ -275,6 +279,7 @@ __global__ __launch_bounds__(masked::kThreads, 1) void masked_attn_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (kh == 0 && t + 1 < nkt) gather(t + 1, 1);
 
     // ---- online softmax per query block over this key half; lane holds keys 16 jb + 4 g + i of
     // query l16, and packs its 8 weights as its own P operand of the P V MFMA (k index 8g+i =
