@@ -255,19 +255,22 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
       const int row = rows[r];
       unsigned char* dst = &sm.kv[bi][(sw * 4 + r) * G::kRowStride];
       if constexpr (F8) {
-        // the row's first 576 bytes by lanes 0-35 (16 bytes each), its 8 scale bytes by lanes
-        // 0-1 (4 bytes each); the other lanes are inactive, so nothing else in the slot is
-        // written. An invalid row is zero-filled when the tile is expanded.
+        // one instruction per row: lanes 0-35 copy its first 576 bytes (16 each); lane 36 copies
+        // bytes 568-583 (the last 8 RoPE bytes once more, then the 8 scale bytes), which land
+        // at slot offset 576, so the scales sit at 584-591 (a separate 4-byte copy of the scales
+        // made FP8 decode calls 3 % slower). The row's start is only 8-byte aligned (584-byte
+        // rows), which 16-byte buffer loads allow. The other lanes are inactive, so nothing else
+        // in the slot is written. An invalid row is zero-filled when the tile is expanded.
         if (row >= 0 && row < T) {
           vbits |= 1u << r;
-          n += 2;
+          n += 1;
           const uint32_t base = (uint32_t)row * kF8Row;
           const uint32_t ldst = lds_addr(dst);
-          if (lane < 36) {
-            if constexpr (NT) dma_lds16_nt(kv8rs, base + 16u * lane, ldst);
-            else dma_lds16(kv8rs, base + 16u * lane, ldst);
+          if (lane < 37) {
+            const uint32_t off = base + (lane < 36 ? 16u * lane : 568u);
+            if constexpr (NT) dma_lds16_nt(kv8rs, off, ldst);
+            else dma_lds16(kv8rs, off, ldst);
           }
-          if (lane < 2) dma_lds4(kv8rs, base + 576u + 4u * lane, ldst + 576u);
         }
       } else if (row >= 0 && row < T) {
         vbits |= 1u << r;
@@ -298,7 +301,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     const bool nope = lane < 56;
     const int roff = nope ? 8 * lane : kF8Nope + 16 * (lane - 56);         // source bytes in the slot
     const int woff = nope ? 16 * lane : 2 * kF8Nope + 16 * (lane - 56);    // bf16 destination
-    const int soff = 576 + (nope ? (lane >> 3) : 0);                       // scale byte
+    const int soff = 584 + (nope ? (lane >> 3) : 0);                       // scale byte
     uint2 lo[4], hi[4];
     unsigned sb[4];
 #pragma unroll
