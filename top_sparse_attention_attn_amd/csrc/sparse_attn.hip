@@ -91,12 +91,11 @@ __device__ __forceinline__ unsigned tile_mask(const Smem<D, HB>& sm, int bi) {
 
 // Output slice of one wave: NB column blocks starting at block DB0.
 template <int D, int HB, int NB>
-__device__ __forceinline__ void pv_step(Smem<D, HB>& sm, f32x4 (&oacc)[HB][NB > 0 ? NB : 1], int db0, int tp, int lane,
-                                        int g, int l16) {
+__device__ __forceinline__ void pv_step(Smem<D, HB>& sm, f32x4 (&oacc)[HB][NB > 0 ? NB : 1], int db0, int tp, int bi,
+                                        int lane, int g, int l16) {
   using G = Geo<D>;
   if constexpr (NB > 0) {
     const int par = tp & 1;
-    const int bi = tp % kBufs;
     if (sm.flag[par][0] | sm.flag[par][1] | sm.flag[par][2] | sm.flag[par][3]) {
 #pragma unroll
       for (int hb = 0; hb < HB; hb++)
@@ -148,6 +147,9 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   const int sw = SCORE ? wave : wave - 4;  // index within the role
   const int db0 = SCORE ? 0 : sw * G::kDBV;
   const bool pv_active = !SCORE && db0 < G::kNDB;
+  // Ring slot of tile t. One token per batch (decode): tiles start at slot 2, so that slots 0-1 can
+  // stage the queries while the first two tiles land.
+  auto slot = [](int t) { return (t + (NT ? 2 : 0)) % kBufs; };
 
   int pair = xcd_local_id(blockIdx.x, gridDim.x, nxcc);
   // One split per token: tokens in a scrambled order (pair * tok_mul mod the token count, tok_mul
@@ -171,42 +173,46 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   const int nq = SCORE ? ((sw + 4 < HB) ? 2 : ((sw < HB) ? 1 : 0)) : 0;
   bf16x8 qreg[QB][SCORE ? G::kDSteps : 1];
   if constexpr (NT) {
-    // One token per batch (decode): every wave copies whole query rows (1 KB per wave instruction
-    // at D = 512) into the row ring, then the score waves read their B operands from there. Loaded
-    // straight into the operand layout (16 rows x 64 bytes per wave instruction) they landed 4.2 us
-    // after the workgroup's start at the decode shape; as whole rows, 2.6 us (operands included),
-    // although the row copies then start only once the queries are out of the ring.
-    static_assert(HP * G::kRowStride <= (int)sizeof(sm.kv), "queries exceed the ring");
-    for (int r = wave; r < HP; r += kThreads / 64) {
-      unsigned char* dst = &sm.kv[0][0] + r * G::kRowStride;
-      if (r < H) {
-        if (lane < G::kLanesPerRow)
-          __builtin_amdgcn_global_load_lds((const void*)(q + ((size_t)tok * H + r) * D + lane * 8), (lds_void_t*)dst, 16,
-                                           0, 0);
-      } else if (lane < G::kLanesPerRow) {
-        *(uint4*)(dst + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    wait_vm_lgkm0<0>();
-    wg_barrier();
+    // One token per batch (decode): each score wave copies the query rows of one of its head blocks
+    // at a time as whole rows (1 KB per wave instruction at D = 512) into its own 16 rows of ring
+    // slots 0-1, waits for its own copies (no workgroup barrier) and reads its B operands from
+    // there. Meanwhile the value waves' first two tiles land in slots 2-3. Loaded straight into the
+    // operand layout (16 rows x 64 bytes per wave instruction) the queries landed 4.2 us after the
+    // workgroup's start at the decode shape; staged by all waves over the whole ring, 2.6 us, but the
+    // row copies then had to wait for them (FP8 decode calls 2.7 % slower than with this form).
+    static_assert(64 * G::kRowStride <= 2 * G::kBufBytes, "query staging exceeds ring slots 0-1");
     if constexpr (SCORE) {
+      unsigned char* const qst = &sm.kv[0][0] + sw * 16 * G::kRowStride;  // this wave's 16 staging rows
 #pragma unroll
       for (int qi = 0; qi < QB; qi++) {
-        const int hr = (sw + 4 * qi) * 16 + l16;
+        const int hb = sw + 4 * qi;
+        if (qi < nq) {
+          for (int r = 0; r < 16; r++) {
+            const int h = hb * 16 + r;
+            unsigned char* dst = qst + r * G::kRowStride;
+            if (h < H) {
+              if (lane < G::kLanesPerRow)
+                __builtin_amdgcn_global_load_lds((const void*)(q + ((size_t)tok * H + h) * D + lane * 8), (lds_void_t*)dst,
+                                                 16, 0, 0);
+            } else if (lane < G::kLanesPerRow) {
+              *(uint4*)(dst + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+            }
+          }
+          wait_vm_lgkm0<0>();
+        }
 #pragma unroll
         for (int s = 0; s < G::kDSteps; s++) {
           bf16x8 v = {};
-          if (qi < nq) v = *(const bf16x8*)(&sm.kv[0][0] + hr * G::kRowStride + 64 * s + 16 * g);
+          if (qi < nq) v = *(const bf16x8*)(qst + l16 * G::kRowStride + 64 * s + 16 * g);
           qreg[qi][s] = v;
         }
         if (g == 0 && qi < nq) {
-          sm.mref[(sw + 4 * qi) * 16 + l16] = kNegInf;
-          sm.lsum[(sw + 4 * qi) * 16 + l16] = 0.f;
+          sm.mref[hb * 16 + l16] = kNegInf;
+          sm.lsum[hb * 16 + l16] = 0.f;
         }
+        wait_lgkm0();  // operands in registers before the rows are staged again
       }
-      wait_lgkm0();
     }
-    wg_barrier();  // the ring is free again for the row gather
   } else if constexpr (SCORE) {
     // Several tokens per batch (prefill): the queries go straight into the operand layout, beside
     // the first row copies (staging them in the ring delays those copies: prefill 1.4 % slower).
@@ -247,7 +253,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     }
   };
   auto issue = [&](int tt, const int (&rows)[4]) -> int {  // returns DMA instructions issued
-    const int bi = tt % kBufs;
+    const int bi = slot(tt);
     unsigned vbits = 0;
     int n = 0;
 #pragma unroll
@@ -296,7 +302,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   // scale byte and converts; the RoPE lanes keep the raw bytes. Called once the tile's copies
   // have landed (this wave's own rows).
   auto expand = [&](int tt) {
-    const int bi = tt % kBufs;
+    const int bi = slot(tt);
     const unsigned vbits = __builtin_amdgcn_readfirstlane((unsigned)sm.vmb[bi][sw]);
     const bool nope = lane < 56;
     const int roff = nope ? 8 * lane : kF8Nope + 16 * (lane - 56);         // source bytes in the slot
@@ -372,9 +378,9 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     f32x4 sacc[QB][2];
     unsigned vm = 0u;
     if constexpr (SCORE) {
-      if (tt < ntl) vm = tile_mask(sm, tt % kBufs);
+      if (tt < ntl) vm = tile_mask(sm, slot(tt));
       if (vm != 0u && nq > 0) {
-        const unsigned char* buf = sm.kv[tt % kBufs];
+        const unsigned char* buf = sm.kv[slot(tt)];
 #pragma unroll
         for (int qi = 0; qi < QB; qi++) sacc[qi][0] = sacc[qi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         // K operands in the order k = 2s + jb (step s over the head dimension, 16-row block jb),
@@ -497,7 +503,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
       }
       if (tt >= 1 && pv_active) {
         const int tp = tt - 1;
-        if (tile_mask(sm, tp % kBufs) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, lane, g, l16);
+        if (tile_mask(sm, slot(tp)) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, slot(tp), lane, g, l16);
       }
       // Index loads of tile tt+3 go out after PV: scalar loads share the LDS wait counter, so
       // issued earlier they would hold up every LDS wait of PV. Their latency overlaps this
