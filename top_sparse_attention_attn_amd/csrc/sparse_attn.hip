@@ -488,10 +488,14 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     }
     // ---- P V for the previous tile (value waves)
     if constexpr (!SCORE) {
+      if (tt >= 1 && pv_active) {
+        const int tp = tt - 1;
+        if (tile_mask(sm, slot(tp)) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, slot(tp), lane, g, l16);
+      }
       if constexpr (F8) {
-        // expand tile tt+1 for the next barrier, before P V so that its LDS round trips overlap
-        // the score waves' work: its copies (issued one tile ago) have landed once at most this
-        // iteration's copies are outstanding
+        // expand tile tt+1 for the next barrier, after P V (its copies, issued one tile ago, have
+        // landed by then, once at most this iteration's copies are outstanding; before P V the
+        // wait for them measured 0.5 % slower)
         if (tt + 1 < ntl) {
           wait_vm_lgkm0_dyn(dma_new);
           // the expansion is on this wave's path to the next barrier: it outranks the score
@@ -500,10 +504,6 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
           expand(tt + 1);
           __builtin_amdgcn_s_setprio(0);
         }
-      }
-      if (tt >= 1 && pv_active) {
-        const int tp = tt - 1;
-        if (tile_mask(sm, slot(tp)) != 0u) pv_step<D, HB, NB>(sm, oacc, db0, tp, slot(tp), lane, g, l16);
       }
       // Index loads of tile tt+3 go out after PV: scalar loads share the LDS wait counter, so
       // issued earlier they would hold up every LDS wait of PV. Their latency overlaps this
