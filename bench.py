@@ -214,18 +214,15 @@ def main():
             x = sets[i % nsets]
             attn(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
 
+        split_phase = sa.sparse_attn_fp8_split if fp8 else sa.sparse_attn_split
+
         def kernel_step(i):  # the main kernel alone (the first of the call's two phases)
             x = sets[i % nsets]
-            sa.sparse_attn_split(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
-
-        if fp8:  # no split-phase entry for FP8 rows: the whole call stands for the kernel
-            kernel_step = step
+            split_phase(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
 
         hb = 1 if cfg.H <= 16 else (2 if cfg.H <= 32 else (4 if cfg.H <= 64 else 8))
-        kernel_name = f"sparse_attn_kernel<{cfg.D},{hb},fp8> + merge" if fp8 else f"sparse_attn_kernel<{cfg.D},{hb}>"
+        kernel_name = f"sparse_attn_kernel<{cfg.D},{hb},fp8>" if fp8 else f"sparse_attn_kernel<{cfg.D},{hb}>"
         work = [sparse_work(x, nsplit, 584 if fp8 else None) for x in sets]
-        if fp8:  # the whole call is timed as the kernel: count its output too
-            work = [(w[0], w[1], w[0]) for w in work]
         units_per_step = cfg.B * cfg.S
         unit = "query-tokens/s"
         bound = "hbm" if args.config in ("decode", "decode_fp8", "ragged", "tiny") else "mfma"

@@ -159,6 +159,23 @@ int sparse_attn_fp8_fwd(const void* q, const void* kv8, const float* attn_sink, 
                         int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int num_splits,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The two phases of sparse_attn_fp8_fwd, as sparse_attn_split_fwd and
+ * sparse_attn_merge_fwd are of sparse_attn_fwd: the split phase leaves the same
+ * partials (O_p, m_p, l_p) in the workspace, and the merge phase combines them
+ * into `out` with the sink added once ("DeepSeek V4 源码剖析", ch. 5, section
+ * 5.5). Both take exactly sparse_attn_fp8_fwd's arguments and checks; call them
+ * in this order on one stream with the same arguments and workspace. When the
+ * split count resolves to 1, the split phase writes `out` in full and the merge
+ * phase does nothing.
+ */
+int sparse_attn_fp8_split_fwd(const void* q, const void* kv8, const float* attn_sink, const int32_t* topk_idxs,
+                              void* out, int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale,
+                              int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+int sparse_attn_fp8_merge_fwd(const void* q, const void* kv8, const float* attn_sink, const int32_t* topk_idxs,
+                              void* out, int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale,
+                              int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Bit-packed top-k mask.                                                    */
 /* Shape rule and row layout: prhub summary of vLLM PR #52217, key source    */

@@ -90,3 +90,18 @@ def test_fp8_decode_config_sampled(oracle_impl):
     ref = oracle_impl.sparse_attn_fp8(bits(q_s), kv8[toks].cpu().numpy(), inp["attn_sink"].cpu().numpy(),
                                       idx_s.numpy(), inp["scale"])
     assert_close(to64(out[toks]).reshape(ref.shape), ref, "fp8 decode")
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_fp8_split_then_merge_equals_one_call(splits):
+    """sparse_attn_fp8_split_fwd then sparse_attn_fp8_merge_fwd give exactly the one-call result."""
+    B, S, H, T, K = 16, 1, 128, 600, 512
+    q, kv8, sink, idx = _case(B, S, H, T, K, seed=61)
+    q, kv8, sink, idx = q.to(DEV), kv8.to(DEV), sink.to(DEV), idx.to(DEV)
+    ws = sa.new_workspace(sa.sparse_attn_workspace_bytes(B, S, H, 512, K, splits), DEV)
+    a = sa.sparse_attn_fp8(q, kv8, sink, idx, 512 ** -0.5, num_splits=splits, workspace=ws)
+    b = torch.full_like(a, 7.0)
+    sa.sparse_attn_fp8_split(q, kv8, sink, idx, 512 ** -0.5, out=b, num_splits=splits, workspace=ws)
+    sa.sparse_attn_fp8_merge(q, kv8, sink, idx, 512 ** -0.5, out=b, num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

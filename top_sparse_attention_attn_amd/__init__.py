@@ -16,6 +16,8 @@ from .api import (  # noqa: F401
     new_workspace,
     sparse_attn,
     sparse_attn_fp8,
+    sparse_attn_fp8_merge,
+    sparse_attn_fp8_split,
     sparse_attn_merge,
     sparse_attn_noalloc,
     sparse_attn_split,

@@ -23,7 +23,8 @@ SA_STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_ALIGN",
 
 EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_fwd",
             "sparse_attn_fwd_noalloc",
-            "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "sparse_attn_fp8_fwd", "topk_bitmask_shape", "topk_bitmask_build",
+            "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "sparse_attn_fp8_fwd", "sparse_attn_fp8_split_fwd",
+            "sparse_attn_fp8_merge_fwd", "topk_bitmask_shape", "topk_bitmask_build",
             "masked_attn_fwd", "masked_attn_offset_fwd", "candidate_mask_apply", "candidate_mask_grid"]
 
 
@@ -58,8 +59,9 @@ def _load():
             getattr(lib, name).restype = I
         lib.sparse_attn_fwd_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I, P]
         lib.sparse_attn_fwd_noalloc.restype = I
-        lib.sparse_attn_fp8_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
-        lib.sparse_attn_fp8_fwd.restype = I
+        for name in ("sparse_attn_fp8_fwd", "sparse_attn_fp8_split_fwd", "sparse_attn_fp8_merge_fwd"):
+            getattr(lib, name).argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
+            getattr(lib, name).restype = I
         lib.topk_bitmask_shape.argtypes = [I64, I64, I64, I, P]
         lib.topk_bitmask_shape.restype = I
         lib.topk_bitmask_build.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P]
@@ -194,9 +196,20 @@ def sparse_attn_fp8(q: torch.Tensor, kv8: torch.Tensor, attn_sink: torch.Tensor,
     return _sparse_call("sparse_attn_fp8_fwd", q, kv8, attn_sink, topk_idxs, scale, out, num_splits, workspace)
 
 
+def sparse_attn_fp8_split(q, kv8, attn_sink, topk_idxs, scale, out=None, num_splits: int = 0, workspace=None):
+    """First phase of sparse_attn_fp8 (sparse_attn_fp8_split_fwd): split partials into `workspace`,
+    or the full output when the call has one split. Pass the same workspace to sparse_attn_fp8_merge."""
+    return _sparse_call("sparse_attn_fp8_split_fwd", q, kv8, attn_sink, topk_idxs, scale, out, num_splits, workspace)
+
+
+def sparse_attn_fp8_merge(q, kv8, attn_sink, topk_idxs, scale, out, num_splits: int = 0, workspace=None):
+    """Second phase of sparse_attn_fp8 (sparse_attn_fp8_merge_fwd): merge the partials into `out`."""
+    return _sparse_call("sparse_attn_fp8_merge_fwd", q, kv8, attn_sink, topk_idxs, scale, out, num_splits, workspace)
+
+
 def _sparse_call(entry, q, kv, attn_sink, topk_idxs, scale, out, num_splits, workspace):
     dev = q.device
-    fp8 = entry == "sparse_attn_fp8_fwd"
+    fp8 = entry.startswith("sparse_attn_fp8_")
     _check(q, "q", torch.bfloat16)
     _check(kv, "kv", torch.uint8 if fp8 else torch.bfloat16, dev)
     _check(attn_sink, "attn_sink", torch.float32, dev)

@@ -178,6 +178,20 @@ int sparse_attn_fp8_fwd(const void* q, const void* kv8, const float* attn_sink, 
                          workspace_bytes, stream, 3, 1);
 }
 
+int sparse_attn_fp8_split_fwd(const void* q, const void* kv8, const float* attn_sink, const int32_t* topk_idxs,
+                              void* out, int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale,
+                              int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attn_run(q, kv8, attn_sink, topk_idxs, out, B, S, H, 512, T, K, scale, num_splits, workspace,
+                         workspace_bytes, stream, 1, 1);
+}
+
+int sparse_attn_fp8_merge_fwd(const void* q, const void* kv8, const float* attn_sink, const int32_t* topk_idxs,
+                              void* out, int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale,
+                              int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attn_run(q, kv8, attn_sink, topk_idxs, out, B, S, H, 512, T, K, scale, num_splits, workspace,
+                         workspace_bytes, stream, 2, 1);
+}
+
 int topk_bitmask_shape(int64_t B, int64_t max_q_len, int64_t max_key_len, int reserve_key_start_word,
                        int64_t* out_shape) {
   if (!out_shape) return SA_ERR_NULL;
