@@ -74,6 +74,36 @@ def test_small_dense_and_null_mask(oracle_impl):
     assert_close(to64(b), ref, "dense")
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_late_maximum_jump(oracle_impl, masked):
+    """Each query's key row equals that query in a late key tile (past the first 64 keys, in
+    either key half), so its logit maximum jumps after the first tiles and the accumulators of
+    that key half must be rescaled; with N(0,1) data the maximum never moves that far."""
+    inp, cfg, mask = _small(33, orc=oracle_impl)
+    q, k = inp["q"].clone(), inp["k"].clone()
+    for b in range(cfg.B):
+        for i in range(cfg.Q):
+            key = 64 + (i * 37 + b * 11) % (cfg.KV - 64)
+            for h in range(cfg.H):
+                k[b, key, h] = q[b, i, h]
+    inp = dict(inp, q=q, k=k)
+    if not masked:
+        mask = None
+    else:  # the jump key is visible in every row
+        m = mask.clone().view(torch.int32)
+        for b in range(cfg.B):
+            for i in range(cfg.Q):
+                key = 64 + (i * 37 + b * 11) % (cfg.KV - 64)
+                w = m[b, i, key // 32].item() & 0xFFFFFFFF
+                w |= 1 << (key % 32)
+                m[b, i, key // 32] = w - (1 << 32) if w >= (1 << 31) else w
+        mask = m
+    out = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"])
+    torch.cuda.synchronize()
+    ref = _ref(oracle_impl, inp, mask).reshape(cfg.B, cfg.Q, cfg.H, cfg.Dv)
+    assert_close(to64(out), ref, f"late jump masked={masked}")
+
+
 def test_load_widths_bitwise_identical():
     inp, cfg, mask = _small(33)
     a = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"], mask_load_bits=128)

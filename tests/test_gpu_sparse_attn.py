@@ -46,6 +46,46 @@ def test_shapes_and_splits(oracle_impl, D, H, splits):
     assert_close(to64(out).reshape(ref.shape), ref, f"D={D} H={H} splits={splits}")
 
 
+@pytest.mark.parametrize("S,splits", [(1, 1), (1, 4), (2, 1)])
+def test_late_maximum_jump_every_head(oracle_impl, S, splits):
+    """Each head's query equals one gathered row that sits in a late tile, so that head's logit
+    maximum jumps by ~33 (log2 units) after its first tiles and the accumulators must be rescaled
+    (the lazily moved reference maximum). Every head position of a head block and both head
+    blocks of a score wave take the jump, at tiles that differ between heads, and the output is
+    then dominated by that one row. With N(0,1) data the reference maximum never moves after the
+    first tile, so this is the only path that exercises the rescale."""
+    B, H, D, T, K = 2, 128, 512, 600, 256  # 8 tiles: 2 per split at 4 splits
+    g = torch.Generator().manual_seed(123 + S + splits)
+    kv = torch.randn(B, T, D, generator=g).to(torch.bfloat16)
+    idx = torch.stack([torch.randperm(T, generator=g)[:K] for _ in range(B * S)]).view(B, S, K).to(torch.int32)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    for b in range(B):
+        for s_ in range(S):
+            for h in range(H):
+                tile = 1 + 2 * ((h + s_) % 4)              # the second tile of one of the 4 ranges
+                slot = tile * 32 + (h * 7 + b) % 32
+                q[b, s_, h] = kv[b, int(idx[b, s_, slot])]
+    sink = torch.randn(H, generator=g)
+    inp = {"q": q.to(DEV), "kv": kv.to(DEV), "attn_sink": sink.to(DEV), "topk_idxs": idx.to(DEV), "scale": D ** -0.5}
+    out = _run(inp, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, f"late jump S={S} splits={splits}")
+
+
+@pytest.mark.parametrize("H", [72, 100])
+@pytest.mark.parametrize("S,splits", [(1, 0), (1, 1), (2, 3)])
+def test_padded_head_blocks(oracle_impl, H, S, splits):
+    """Head counts that are not a multiple of 16 in the eight-head-block form: the padded heads
+    (72 or 100 .. 127) have zero queries, are computed and never written; one token per batch
+    (the decode form, queries staged per score wave) and two, with and without splits."""
+    inp = _custom(3, S, H, 512, 400, 300, seed=90 + H + S + splits)
+    out = _run(inp, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, f"H={H} S={S} splits={splits}")
+
+
 @pytest.mark.parametrize("K", [0, 1, 31, 33])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_few_slots(oracle_impl, K, splits):

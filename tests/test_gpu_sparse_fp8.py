@@ -105,3 +105,13 @@ def test_fp8_split_then_merge_equals_one_call(splits):
     sa.sparse_attn_fp8_merge(q, kv8, sink, idx, 512 ** -0.5, out=b, num_splits=splits, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("num_splits", [1, 4])
+def test_fp8_padded_head_blocks(oracle_impl, num_splits):
+    """H = 100 (eight head blocks, heads 100 .. 127 padded) over FP8 rows, one token per batch."""
+    B, S, H, T, K = 3, 1, 100, 300, 200
+    q, kv8, sink, idx = _case(B, S, H, T, K, seed=71)
+    out = _run(q, kv8, sink, idx, 512 ** -0.5, num_splits=num_splits)
+    ref = oracle_impl.sparse_attn_fp8(bits(q), kv8.numpy(), sink.numpy(), idx.numpy(), 512 ** -0.5)
+    assert_close(to64(out).reshape(ref.shape), ref, f"fp8 H=100 splits={num_splits}")

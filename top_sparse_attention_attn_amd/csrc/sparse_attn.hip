@@ -482,8 +482,11 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
             }
           }
         }
-        // Every score wave publishes its own rescale flag for this tile (no shared writes).
-        if (lane == 0) sm.flag[par][sw] = __any(any_resc) ? 1 : 0;
+        // Every score wave publishes its own rescale flag for this tile (no shared writes). The
+        // vote is taken with every lane active: a vote inside the lane-0 branch would see lane 0
+        // (the heads of lane column 0) only.
+        const bool resc_wave = __any(any_resc);
+        if (lane == 0) sm.flag[par][sw] = resc_wave ? 1 : 0;
       }
     }
     // ---- P V for the previous tile (value waves)
