@@ -104,6 +104,26 @@ def test_late_maximum_jump(oracle_impl, masked):
     assert_close(to64(out), ref, f"late jump masked={masked}")
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_rising_maximum_every_tile(oracle_impl, masked):
+    """Keys whose logit with every query rises by ~10 (log2 units) from one 64-key tile to the next,
+    so each key half's reference maximum moves and its accumulators are rescaled at every tile."""
+    inp, cfg, mask = _small(34, orc=oracle_impl)
+    g = torch.Generator().manual_seed(34)
+    D = cfg.Dqk
+    u = torch.randn(D, generator=g)
+    u = u / u.norm()
+    q = (torch.randn(cfg.B, cfg.Q, cfg.H, D, generator=g) * 0.05 + 4.0 * u).to(torch.bfloat16)
+    step = 10.0 / 1.4426950408889634 * D ** 0.5 / 4.0
+    tiles = (torch.arange(cfg.KV) // 64).to(torch.float32)
+    k = (torch.randn(cfg.B, cfg.KV, cfg.H, D, generator=g) * 0.05 + tiles[None, :, None, None] * step * u).to(torch.bfloat16)
+    inp = dict(inp, q=q.to(DEV), k=k.to(DEV))
+    out = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask if masked else None, inp["scale"])
+    torch.cuda.synchronize()
+    ref = _ref(oracle_impl, inp, mask if masked else None).reshape(cfg.B, cfg.Q, cfg.H, cfg.Dv)
+    assert_close(to64(out), ref, f"rising maximum masked={masked}")
+
+
 def test_load_widths_bitwise_identical():
     inp, cfg, mask = _small(33)
     a = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, inp["scale"], mask_load_bits=128)

@@ -46,16 +46,17 @@ def test_shapes_and_splits(oracle_impl, D, H, splits):
     assert_close(to64(out).reshape(ref.shape), ref, f"D={D} H={H} splits={splits}")
 
 
-@pytest.mark.parametrize("S,splits", [(1, 1), (1, 4), (2, 1)])
-def test_late_maximum_jump_every_head(oracle_impl, S, splits):
+@pytest.mark.parametrize("S,splits,H,D", [(1, 1, 128, 512), (1, 4, 128, 512), (2, 1, 128, 512), (1, 4, 40, 512),
+                                         (2, 1, 16, 512), (1, 1, 100, 64)])
+def test_late_maximum_jump_every_head(oracle_impl, S, splits, H, D):
     """Each head's query equals one gathered row that sits in a late tile, so that head's logit
     maximum jumps by ~33 (log2 units) after its first tiles and the accumulators must be rescaled
     (the lazily moved reference maximum). Every head position of a head block and both head
     blocks of a score wave take the jump, at tiles that differ between heads, and the output is
     then dominated by that one row. With N(0,1) data the reference maximum never moves after the
     first tile, so this is the only path that exercises the rescale."""
-    B, H, D, T, K = 2, 128, 512, 600, 256  # 8 tiles: 2 per split at 4 splits
-    g = torch.Generator().manual_seed(123 + S + splits)
+    B, T, K = 2, 600, 256  # 8 tiles: 2 per split at 4 splits
+    g = torch.Generator().manual_seed(123 + S + splits + H + D)
     kv = torch.randn(B, T, D, generator=g).to(torch.bfloat16)
     idx = torch.stack([torch.randperm(T, generator=g)[:K] for _ in range(B * S)]).view(B, S, K).to(torch.int32)
     q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
@@ -70,7 +71,34 @@ def test_late_maximum_jump_every_head(oracle_impl, S, splits):
     out = _run(inp, num_splits=splits)
     torch.cuda.synchronize()
     ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
-    assert_close(to64(out).reshape(ref.shape), ref, f"late jump S={S} splits={splits}")
+    assert_close(to64(out).reshape(ref.shape), ref, f"late jump S={S} splits={splits} H={H} D={D}")
+
+
+@pytest.mark.parametrize("S,splits", [(1, 1), (2, 1), (1, 2)])
+def test_rising_maximum_every_tile(oracle_impl, S, splits):
+    """Rows whose logit with every head rises by ~10 (log2 units) from one 32-row tile to the next,
+    so the reference maximum moves and the accumulators are rescaled at every tile (weights of the
+    earlier tiles fall by 2^-10 each time)."""
+    B, H, D, T, K = 1, 128, 512, 400, 256
+    g = torch.Generator().manual_seed(131 + S + splits)
+    u = torch.randn(D, generator=g)
+    u = u / u.norm()
+    q = (torch.randn(B, S, H, D, generator=g) * 0.05 + 4.0 * u).to(torch.bfloat16)
+    kv = (torch.randn(B, T, D, generator=g) * 0.05).to(torch.float32)
+    idx = torch.stack([torch.randperm(T, generator=g)[:K] for _ in range(B * S)]).view(B, S, K).to(torch.int32)
+    # row of slot k: its component along u grows with the slot's tile, so logit ~ 4 * c_t / sqrt(D)
+    step = 10.0 / 1.4426950408889634 * D ** 0.5 / 4.0  # ~10 log2 units per tile
+    for s_ in range(S):
+        for k in range(K):
+            r = int(idx[0, s_, k])
+            kv[0, r] = kv[0, r] * 0 + torch.randn(D, generator=g) * 0.05 + (k // 32) * step * u
+    kv = kv.to(torch.bfloat16)
+    sink = torch.randn(H, generator=g)
+    inp = {"q": q.to(DEV), "kv": kv.to(DEV), "attn_sink": sink.to(DEV), "topk_idxs": idx.to(DEV), "scale": D ** -0.5}
+    out = _run(inp, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, f"rising maximum S={S} splits={splits}")
 
 
 @pytest.mark.parametrize("H", [72, 100])
