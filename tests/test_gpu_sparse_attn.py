@@ -101,6 +101,19 @@ def test_rising_maximum_every_tile(oracle_impl, S, splits):
     assert_close(to64(out).reshape(ref.shape), ref, f"rising maximum S={S} splits={splits}")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.05, 0.3])
+@pytest.mark.parametrize("S,splits", [(1, 4), (2, 1)])
+def test_scale_signs(oracle_impl, scale, S, splits):
+    """A zero scale (every valid slot weighs the same), a negative one (the order of the logits
+    reversed) and a large one, with and without splits."""
+    inp = _custom(2, S, 128, 512, 400, 300, seed=140 + S + splits)
+    inp["scale"] = scale
+    out = _run(inp, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, f"scale={scale} S={S} splits={splits}")
+
+
 @pytest.mark.parametrize("H", [72, 100])
 @pytest.mark.parametrize("S,splits", [(1, 0), (1, 1), (2, 3)])
 def test_padded_head_blocks(oracle_impl, H, S, splits):
