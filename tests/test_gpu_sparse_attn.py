@@ -35,7 +35,7 @@ def test_tiny_config(oracle_impl):
     assert_close(to64(out).reshape(ref.shape), ref, "tiny")
 
 
-@pytest.mark.parametrize("D,H", [(64, 8), (64, 40), (512, 16), (512, 128)])
+@pytest.mark.parametrize("D,H", [(64, 1), (64, 8), (64, 40), (512, 1), (512, 16), (512, 128)])
 @pytest.mark.parametrize("splits", [1, 3])
 def test_shapes_and_splits(oracle_impl, D, H, splits):
     # K = 200 spans several 32-row tiles and ends in a ragged tile; splits > 1 exercise the combine.
