@@ -39,7 +39,7 @@ typedef enum {
   SA_ERR_NULL = 1,        /* a required pointer is NULL */
   SA_ERR_SHAPE = 2,       /* a size is negative or sizes are inconsistent */
   SA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
-  SA_ERR_UNSUPPORTED = 4, /* a head dimension / head count this build has no kernel for */
+  SA_ERR_UNSUPPORTED = 4, /* a head dimension / head count the library has no kernel for */
   SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
   SA_ERR_HIP = 6          /* a HIP call (launch) failed */
 } sa_status;

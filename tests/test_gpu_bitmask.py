@@ -66,7 +66,7 @@ def test_single_equals_batched():
 
 def test_index_list_4byte_aligned(oracle_impl):
     """topk a multiple of 4 but the index list only 4-byte aligned (a view one int32 into a
-    buffer): the build reads it with 4-byte loads and gives the same bits as an aligned copy."""
+    buffer): the mask builder reads it with 4-byte loads and gives the same bits as an aligned copy."""
     B, Q, topk, key_len = 2, 100, 64, 3000
     g = torch.Generator().manual_seed(77)
     src = torch.randint(-1, key_len + 5, (B, Q, topk), generator=g, dtype=torch.int32)
