@@ -410,3 +410,54 @@ def test_split_merge_many_tokens(oracle_impl):
     got = to64(out.reshape(B * S, H, D)[torch.as_tensor(tokens, device=DEV)])
     assert_close(got, ref, "4100 tokens, 2 splits")
 
+
+
+def _random_case(rng: np.random.Generator):
+    """One random shape and data mode: N(0,1), queries equal to gathered rows (late maximum jumps),
+    heavy duplicates, most slots empty, or all heads' logits shifted by a large common offset."""
+    D = int(rng.choice([64, 512]))
+    H = int(rng.choice([1, 5, 16, 33, 64, 100, 128]))
+    B, S = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    T = int(rng.integers(1, 700))
+    K = int(rng.integers(0, 400))
+    splits = int(rng.choice([0, 1, 2, 3, 7, 16]))
+    mode = rng.choice(["normal", "aligned", "dups", "holes", "offset"])
+    g = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+    q = torch.randn(B, S, H, D, generator=g)
+    kv = torch.randn(B, T, D, generator=g)
+    idx = torch.randint(0, T, (B, S, K), generator=g, dtype=torch.int32)
+    if mode == "dups" and K > 0:
+        idx = idx % max(1, min(T, 3))
+    if mode == "holes":
+        idx[torch.rand(B, S, K, generator=g) < 0.9] = -1
+    else:
+        idx[torch.rand(B, S, K, generator=g) < 0.05] = -1
+    if mode == "aligned" and K > 0:
+        for b in range(B):
+            for s_ in range(S):
+                for h in range(H):
+                    k = int(torch.randint(0, K, (1,), generator=g))
+                    r = int(idx[b, s_, k])
+                    if r >= 0:
+                        q[b, s_, h] = kv[b, r]
+    if mode == "offset":
+        u = torch.randn(D, generator=g)
+        kv = kv + 3.0 * u / u.norm()
+        q = q + 3.0 * u / u.norm()
+    sink = torch.randn(H, generator=g) * 2
+    scale = float(rng.choice([D ** -0.5, 0.02, 0.3]))
+    inp = {"q": q.to(torch.bfloat16).to(DEV), "kv": kv.to(torch.bfloat16).to(DEV), "attn_sink": sink.to(DEV),
+           "topk_idxs": idx.to(DEV), "scale": scale}
+    return inp, splits, f"B={B} S={S} H={H} D={D} T={T} K={K} splits={splits} mode={mode} scale={scale:.3g}"
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_and_data(oracle_impl, seed):
+    """Randomised shapes, split counts and data modes against the oracle (fixed seeds, 8 cases each)."""
+    rng = np.random.default_rng(1000 + seed)
+    for _ in range(8):
+        inp, splits, what = _random_case(rng)
+        out = _run(inp, num_splits=splits)
+        torch.cuda.synchronize()
+        ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+        assert_close(to64(out).reshape(ref.shape), ref, what)
