@@ -371,3 +371,39 @@ def test_masked_graph_replay_tracks_new_masks(oracle_impl):
         torch.cuda.synchronize()
         ref = _ref(oracle_impl, inp, mask).reshape(cfg.B, cfg.Q, cfg.H, cfg.Dv)
         assert_close(to64(out), ref, f"masked replay {rep}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes_and_data(oracle_impl, seed):
+    """Randomised shapes, masks (top-k lists of random length, or none) and data modes (N(0,1),
+    keys equal to queries, a large common logit offset) against the oracle; 16- and 4-byte mask
+    loads bitwise equal. Fixed seeds, 6 cases each."""
+    rng = np.random.default_rng(2000 + seed)
+    for _ in range(6):
+        B, Q, KV, H = int(rng.integers(1, 3)), int(rng.integers(1, 300)), int(rng.integers(1, 400)), int(rng.integers(1, 5))
+        mode = rng.choice(["normal", "aligned", "offset"])
+        g = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+        q = torch.randn(B, Q, H, 192, generator=g)
+        k = torch.randn(B, KV, H, 192, generator=g)
+        v = torch.randn(B, KV, H, 128, generator=g)
+        if mode == "aligned":
+            for b in range(B):
+                for i in range(Q):
+                    k[b, int(rng.integers(KV))] = q[b, i]
+        if mode == "offset":
+            u = torch.randn(192, generator=g)
+            q, k = q + 3.0 * u / u.norm(), k + 3.0 * u / u.norm()
+        topk = int(rng.integers(0, KV + 1))
+        idx = torch.stack([torch.randperm(KV, generator=g)[:topk] for _ in range(B * Q)]).view(B, Q, topk).to(torch.int32)
+        mask = None if rng.random() < 0.25 else _oracle_mask(oracle_impl, idx, KV)
+        scale = float(rng.choice([192 ** -0.5, 0.02, 0.3]))
+        inp = {"q": q.to(torch.bfloat16).to(DEV), "k": k.to(torch.bfloat16).to(DEV), "v": v.to(torch.bfloat16).to(DEV),
+               "scale": scale}
+        out = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, scale)
+        if mask is not None:
+            out32 = sa.masked_attn(inp["q"], inp["k"], inp["v"], mask, scale, mask_load_bits=32)
+            torch.cuda.synchronize()
+            assert torch.equal(out, out32)
+        torch.cuda.synchronize()
+        ref = _ref(oracle_impl, inp, mask).reshape(B, Q, H, 128)
+        assert_close(to64(out), ref, f"B={B} Q={Q} KV={KV} H={H} topk={topk} mode={mode} mask={mask is not None}")

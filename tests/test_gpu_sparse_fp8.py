@@ -115,3 +115,22 @@ def test_fp8_padded_head_blocks(oracle_impl, num_splits):
     out = _run(q, kv8, sink, idx, 512 ** -0.5, num_splits=num_splits)
     ref = oracle_impl.sparse_attn_fp8(bits(q), kv8.numpy(), sink.numpy(), idx.numpy(), 512 ** -0.5)
     assert_close(to64(out).reshape(ref.shape), ref, f"fp8 H=100 splits={num_splits}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_fp8_random_shapes_equal_bf16_on_dequantized_rows(oracle_impl, seed):
+    """Randomised batch, token, head, row and slot counts and split choices: the FP8 call is bitwise
+    the bf16 call on the oracle's dequantized rows (6 cases per seed)."""
+    rng = np.random.default_rng(3000 + seed)
+    for _ in range(6):
+        B, S, H = int(rng.integers(1, 4)), int(rng.integers(1, 3)), int(rng.choice([1, 16, 40, 100, 128]))
+        T, K = int(rng.integers(1, 600)), int(rng.integers(0, 400))
+        splits = int(rng.choice([0, 1, 3, 8]))
+        q, kv8, sink, idx = _case(B, S, H, max(T, 1), 0, seed=int(rng.integers(1 << 30)))
+        g = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+        idx = torch.randint(-1, T, (B, S, K), generator=g, dtype=torch.int32)
+        deq = torch.from_numpy(oracle_impl.fp8_dequant(kv8.numpy())).to(torch.bfloat16)
+        a = _run(q, kv8, sink, idx, 512 ** -0.5, num_splits=splits)
+        b = sa.sparse_attn(q.to(DEV), deq.to(DEV), sink.to(DEV), idx.to(DEV), 512 ** -0.5, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (B, S, H, T, K, splits)
