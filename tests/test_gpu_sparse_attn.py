@@ -334,6 +334,34 @@ def test_ragged_config_sampled(oracle_impl):
     del inp
 
 
+@pytest.mark.parametrize("B,S,splits", [(2, 1, 0), (1, 2, 1), (1, 1, 4)])
+def test_rows_past_4gb(oracle_impl, B, S, splits):
+    """bf16 rows at D = 512 more than 4 GB into a batch (2^22 rows per 4 GB): rows on both sides
+    of each 4 GB mark, the batch's last row and, with B = 2, a second batch that starts past 4 GB,
+    against the oracle on the gathered rows."""
+    H, D, K = 16, 512, 320
+    T = (1 << 22) + 3000
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    kv = torch.randn(B, T, D, device=DEV, dtype=torch.bfloat16, generator=gen)
+    g = torch.Generator().manual_seed(78)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16).to(DEV)
+    sink = torch.randn(H, generator=g).to(DEV)
+    mark = 1 << 22
+    fixed = torch.tensor([0, mark - 2, mark - 1, mark, mark + 1, T - 1], dtype=torch.int64)
+    idx = torch.empty(B * S, K, dtype=torch.int64)
+    for t in range(B * S):
+        lo = torch.randperm(mark - 2, generator=g)[: (K - 6) // 2] + 1
+        hi = torch.randperm(T - mark - 2, generator=g)[: K - 6 - (K - 6) // 2] + mark + 2
+        idx[t] = torch.cat([fixed, lo, hi])[torch.randperm(K, generator=g)]
+    idx = idx.view(B, S, K).to(torch.int32).to(DEV)
+    out = sa.sparse_attn(q, kv, sink, idx, D ** -0.5, num_splits=splits)
+    torch.cuda.synchronize()
+    tokens = np.arange(B * S)
+    ref = sparse_reference(oracle_impl, q, kv, sink, idx, D ** -0.5, tokens)
+    assert_close(to64(out.reshape(B * S, H, D)), ref, f"rows past 4 GB B={B} S={S}")
+    del kv
+
+
 def test_graph_replay_tracks_new_indices(oracle_impl):
     """Capture once, replay with new index lists (grid depends only on shapes)."""
     inp = _custom(4, 1, 128, 512, 600, 320, seed=21)
