@@ -79,6 +79,7 @@ struct Smem {
   float fin[HB * 16];
   unsigned char vmb[kBufs][8];  // per value wave: validity of its 4 rows of the tile (one byte each)
   int flag[2][4];
+  int idx[2][64];  // bf16 rows: slot indices of a tile two or three ahead (by tile parity; 32 used)
 };
 
 // 32-bit validity mask of a tile's rows (bit j = row j holds a gathered row).
@@ -168,6 +169,8 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   const __bf16* __restrict__ kv_b = (const __bf16*)kv + (size_t)(F8 ? 0 : b) * T * D;
   static_assert(!F8 || D == 512, "FP8 rows hold D = 512");
   u32x4 kv8rs = {};  // FP8: the batch's rows as a buffer resource
+  // the token's slot indices as a buffer resource (score wave 0 copies them into LDS for bf16 rows)
+  const u32x4 idxrs = buffer_rsrc(idx_tok, (uint32_t)((long)K * 4 < 0xFFFFFFFFl ? (long)K * 4 : 0xFFFFFFFFl));
   u32x4 kvrs = {};   // bf16: the batch's rows from the start, 4 GB reach per resource base (no range check)
   if constexpr (!F8) kvrs = buffer_rsrc(kv_b, 0xFFFFFFFFu);
   if constexpr (F8) kv8rs = buffer_rsrc((const uint8_t*)kv + (size_t)b * T * kF8Row, (uint32_t)T * kF8Row);
@@ -379,13 +382,33 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
 
   for (int tt = 0; tt <= ntl; tt++) {
     // Tile tt's rows have landed once only the younger tile's DMAs may still be pending.
-    if constexpr (SCORE || F8) wait_lgkm0();  // FP8: the tile was expanded (and waited for) before
+    if constexpr (SCORE && !F8) wait_vm_lgkm0<0>();  // score wave 0's index copy has landed
+    else if constexpr (SCORE || F8) wait_lgkm0();  // FP8: the tile was expanded (and waited for) before
     else wait_vm_lgkm0_dyn(tt + 1 < ntl ? dma_last : 0);
     wg_barrier();  // tile tt and P(tt-1) visible; everyone is done with tile tt-2 and P(tt-2)
+    // bf16 rows: score wave 0 copies tile tt+3's 32 slot indices into LDS (4 bytes per lane, waited for
+    // before the next barrier), where the value waves read theirs after that barrier. With the
+    // indices as scalar loads after P V, the value waves waited ~400 cycles for them every tile
+    // (prefill 3 %, ragged decode 1.7 % slower; FP8 rows keep the scalar loads: their value waves
+    // reach the barrier later and measured no gain).
+    if constexpr (SCORE && !F8) {
+      if (sw == 0 && tt + 3 < ntl && lane < 32)
+        dma_lds4(idxrs, (uint32_t)(((t0 + tt + 3) * kTile + lane) * 4), lds_addr(&sm.idx[(tt + 3) & 1][0]));
+    }
     // ---- prefetch tile tt+2 into the buffer freed by tile tt-2
     int dma_new = 0;  // copies issued in this iteration (tile tt+2)
     if constexpr (!SCORE) {
-      if (tt + 2 < ntl) dma_last = dma_new = issue(tt + 2, rows_next);
+      if (tt + 2 < ntl) {
+        if (!F8 && tt > 0) {  // tile 2's indices came in with scalar loads before the loop
+          const int4 v = *(const int4*)&sm.idx[(tt + 2) & 1][4 * sw];
+          const int slot0 = (t0 + tt + 2) * kTile + sw * 4;  // slots at or past K are empty
+          rows_next[0] = slot0 + 0 < K ? __builtin_amdgcn_readfirstlane(v.x) : -1;
+          rows_next[1] = slot0 + 1 < K ? __builtin_amdgcn_readfirstlane(v.y) : -1;
+          rows_next[2] = slot0 + 2 < K ? __builtin_amdgcn_readfirstlane(v.z) : -1;
+          rows_next[3] = slot0 + 3 < K ? __builtin_amdgcn_readfirstlane(v.w) : -1;
+        }
+        dma_last = dma_new = issue(tt + 2, rows_next);
+      }
     }
     // ---- scores of tile tt (score waves)
     f32x4 sacc[QB][2];
@@ -450,18 +473,30 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
           // validity of this lane's rows 4g+i and 16+4g+i: bits i and 16+i of vg (one shift per
           // tile, immediate masks after it)
           const unsigned vg = vm >> (4 * lg);
+          // logits in log2 units, computed in place in the accumulators; empty rows masked to -inf,
+          // skipped when all 32 rows hold a gathered row (every tile at the decode shape)
+#pragma unroll
+          for (int qi = 0; qi < QB; qi++)
+#pragma unroll
+            for (int jb = 0; jb < 2; jb++)
+#pragma unroll
+              for (int i = 0; i < 4; i++) sacc[qi][jb][i] *= scale_log2;
+          if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+            for (int qi = 0; qi < QB; qi++)
+#pragma unroll
+              for (int jb = 0; jb < 2; jb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                  if (!(vg & (1u << (16 * jb + i)))) sacc[qi][jb][i] = kNegInf;
+          }
 #pragma unroll
           for (int qi = 0; qi < QB; qi++) {
-            // logits in log2 units, empty rows masked; computed in place in the accumulators
             float tmax = kNegInf;
 #pragma unroll
             for (int jb = 0; jb < 2; jb++)
 #pragma unroll
-              for (int i = 0; i < 4; i++) {
-                const float v = (vg & (1u << (16 * jb + i))) ? sacc[qi][jb][i] * scale_log2 : kNegInf;
-                sacc[qi][jb][i] = v;
-                tmax = __builtin_elementwise_maximum(tmax, v);
-              }
+              for (int i = 0; i < 4; i++) tmax = __builtin_elementwise_maximum(tmax, sacc[qi][jb][i]);
             tmax = max4_x16_x32(tmax);
             const float mold = mst[qi];
             const bool move = tmax > mold + kLazy;  // also true for the first finite maximum
@@ -521,10 +556,11 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
           __builtin_amdgcn_s_setprio(0);
         }
       }
-      // Index loads of tile tt+3 go out after PV: scalar loads share the LDS wait counter, so
-      // issued earlier they would hold up every LDS wait of PV. Their latency overlaps this
-      // wave's wait at the next barrier.
-      if (tt + 3 < ntl) load_rows(tt + 3, rows_next);
+      // FP8 rows: index loads of tile tt+3 go out after PV (scalar loads share the LDS wait counter,
+      // so issued earlier they would hold up every LDS wait of PV).
+      if constexpr (F8) {
+        if (tt + 3 < ntl) load_rows(tt + 3, rows_next);
+      }
     }
   }
 
