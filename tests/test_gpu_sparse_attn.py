@@ -334,19 +334,19 @@ def test_ragged_config_sampled(oracle_impl):
     del inp
 
 
-@pytest.mark.parametrize("B,S,splits", [(2, 1, 0), (1, 2, 1), (1, 1, 4)])
-def test_rows_past_4gb(oracle_impl, B, S, splits):
-    """bf16 rows at D = 512 more than 4 GB into a batch (2^22 rows per 4 GB): rows on both sides
-    of each 4 GB mark, the batch's last row and, with B = 2, a second batch that starts past 4 GB,
-    against the oracle on the gathered rows."""
-    H, D, K = 16, 512, 320
-    T = (1 << 22) + 3000
+@pytest.mark.parametrize("D,B,S,splits", [(512, 2, 1, 0), (512, 1, 2, 1), (512, 1, 1, 4), (64, 2, 1, 0), (64, 1, 2, 1)])
+def test_rows_past_4gb(oracle_impl, D, B, S, splits):
+    """bf16 rows more than 4 GB into a batch (2^22 rows per 4 GB at D = 512, 2^25 at D = 64): rows
+    on both sides of each 4 GB mark, the batch's last row and, with B = 2, a second batch that
+    starts past 4 GB, against the oracle on the gathered rows."""
+    H, K = 16, 320
+    mark = (1 << 32) // (2 * D)
+    T = mark + 3000
     gen = torch.Generator(device=DEV).manual_seed(77)
     kv = torch.randn(B, T, D, device=DEV, dtype=torch.bfloat16, generator=gen)
     g = torch.Generator().manual_seed(78)
     q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16).to(DEV)
     sink = torch.randn(H, generator=g).to(DEV)
-    mark = 1 << 22
     fixed = torch.tensor([0, mark - 2, mark - 1, mark, mark + 1, T - 1], dtype=torch.int64)
     idx = torch.empty(B * S, K, dtype=torch.int64)
     for t in range(B * S):
@@ -358,7 +358,7 @@ def test_rows_past_4gb(oracle_impl, B, S, splits):
     torch.cuda.synchronize()
     tokens = np.arange(B * S)
     ref = sparse_reference(oracle_impl, q, kv, sink, idx, D ** -0.5, tokens)
-    assert_close(to64(out.reshape(B * S, H, D)), ref, f"rows past 4 GB B={B} S={S}")
+    assert_close(to64(out.reshape(B * S, H, D)), ref, f"rows past 4 GB D={D} B={B} S={S}")
     del kv
 
 
