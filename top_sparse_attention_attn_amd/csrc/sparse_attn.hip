@@ -393,7 +393,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
     // reach the barrier later and measured no gain).
     if constexpr (SCORE && !F8) {
       if (sw == 0 && tt + 3 < ntl && lane < 32)
-        dma_lds4(idxrs, (uint32_t)(((t0 + tt + 3) * kTile + lane) * 4), lds_addr(&sm.idx[(tt + 3) & 1][0]));
+        dma_lds4(idxrs, (uint32_t)((t0 + tt + 3) * kTile + lane) * 4u, lds_addr(&sm.idx[(tt + 3) & 1][0]));
     }
     // ---- prefetch tile tt+2 into the buffer freed by tile tt-2
     int dma_new = 0;  // copies issued in this iteration (tile tt+2)
