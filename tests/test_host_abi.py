@@ -92,6 +92,14 @@ def test_noalloc_rejects_oversize_before_any_hip_call():
 
 def test_workspace_policy():
     assert sa.sparse_attn_num_splits(64, 1, 128, 512, 1152) == 4
+    # the library's split counts at measured decode shapes (each within 3 % of the fastest)
+    for ntok, want in ((8, 9), (16, 8), (24, 7), (32, 6), (40, 6), (48, 5), (80, 3), (96, 2), (128, 2), (192, 1)):
+        assert sa.sparse_attn_num_splits(ntok, 1, 128, 512, 1152) == want, ntok
+    # never more than one workgroup per CU (256) in all, never more than the tiles or 16
+    for ntok in range(1, 300):
+        for K in (1, 32, 100, 512, 1152, 2048, 65536):
+            n = sa.sparse_attn_num_splits(ntok, 1, 128, 512, K)
+            assert 1 <= n <= max(1, min(16, -(-K // 32), 256 // ntok)), (ntok, K, n)
     assert sa.sparse_attn_num_splits(1, 4096, 128, 512, 1152) == 1
     assert sa.sparse_attn_num_splits(1, 4, 8, 64, 32) == 1
     assert sa.sparse_attn_workspace_bytes(1, 4096, 128, 512, 1152) == 0
