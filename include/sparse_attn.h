@@ -75,7 +75,11 @@ size_t sparse_attn_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, i
 /*
  * The split count sparse_attn_fwd uses for num_splits = 0 (each token's K
  * slots are cut into this many contiguous ranges processed by separate
- * workgroups and merged afterwards). Returns 1 for invalid sizes.
+ * workgroups and merged afterwards). It depends on B*S and K only: never more
+ * than 256 workgroups (one per CU) in all, at most K's 32-slot tile count and
+ * 16, and within that the count that balances each workgroup's tile loop
+ * against the partials written and merged (a cost fitted to measured decode
+ * calls). Returns 1 for invalid sizes.
  */
 int sparse_attn_num_splits(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K);
 
