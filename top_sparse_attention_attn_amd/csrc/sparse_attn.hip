@@ -699,13 +699,17 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 // o = sum_p 2^(m_p - M) O_p / (sum_p 2^(m_p - M) l_p + 2^(sink - M)), M the largest term, where
 // split p left its unnormalised output O_p (bf16) and its reference maximum m_p (log2 units)
 // and weight sum l_p.
-// Grid: tokens x head blocks (mapped so a token's blocks run on the XCD that wrote its
-// partials). The block's partials are 16-byte chunks of the MFMA output layout
+// Grid: tokens x head blocks x DS column ranges (mapped so a token's workgroups run on the XCD
+// that wrote its partials). The block's partials are 16-byte chunks of the MFMA output layout
 // [d block][lane][4 heads]; every thread issues all its chunk loads of a group of up to four
 // splits before it waits, then the merged block is staged in LDS and stored row by row.
-// 512 threads (two chunks per thread at D = 512) measured faster than 128, 256 or 1024.
+// With DS = 1, 512 threads (two chunks per thread at D = 512) measured faster than 128, 256 or 1024.
+// With few (token, head block) pairs (at most 320: up to 40 tokens of 128 heads) each block's 512
+// columns are split over DS = 4 workgroups of 128 threads, so that more CUs pull the partials:
+// decode calls 6 % faster at 8 tokens, 3-4.5 % at 12-16, 1-2 % at 20-40; at 96-128 tokens the extra
+// workgroups cost 1.5-3.5 %, and DS = 2 (256 threads) measured 6-9 % slower at 24-32 tokens.
 constexpr int kCombineThreads = 512;
-template <int D, int HB>
+template <int D, int HB, int DS>
 __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(const __bf16* __restrict__ ws_o,
                                                                    const float* __restrict__ ws_ml,
                                                                    const float* __restrict__ sink,
@@ -713,15 +717,19 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
                                                                    int nxcc) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
+  constexpr int NT = kCombineThreads / DS;             // threads of this workgroup
   constexpr int kChunks = G::kNDB * 64 * 8 / 16;       // 16-byte chunks of one partial block
-  constexpr int kPerThread = (kChunks + kCombineThreads - 1) / kCombineThreads;  // chunks per thread
+  constexpr int kChunksW = kChunks / DS;               // ... of this workgroup's column range
+  constexpr int kPerThread = (kChunksW + NT - 1) / NT;  // chunks per thread
   constexpr int kOutStride = D + 8;                    // bf16 per staged output row
   constexpr bool PAIR = G::kDBV % 2 == 0;              // partials stored two d blocks per lane
+  static_assert(DS == 1 || (PAIR && kChunksW % 64 == 0), "column split needs whole d-block pairs");
   __shared__ float wgt[kMaxSplits * 16];
   __shared__ __attribute__((aligned(16))) __bf16 stage[16 * kOutStride];
   const int blk = xcd_local_id(blockIdx.x, gridDim.x, nxcc);
-  const int tok = blk / HB, hb = blk % HB;
+  const int tok = blk / (HB * DS), hb = (blk / DS) % HB, ds = blk % DS;
   const int t = threadIdx.x;
+  const int c0 = ds * kChunksW;                        // first chunk of this workgroup's columns
 
   // PAIR: chunk c of a block is lane c%64 of d-block pair c/64: heads 4*(lane/16)+i, columns
   // (c/64)*32 + lane%16 and 16 more. Otherwise chunk c holds lanes 2(c%32), 2(c%32)+1 of d block
@@ -753,8 +761,8 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
         const uint4* src = (const uint4*)(ws_o + ((size_t)(tok * nsplit + p0 + pp) * HP + hb * 16) * D);
 #pragma unroll
         for (int j = 0; j < kPerThread; j++) {
-          const int c = t + kCombineThreads * j;
-          if (c < kChunks) v[pp][j] = src[c];
+          const int c = c0 + t + NT * j;
+          if (c < c0 + kChunksW) v[pp][j] = src[c];
         }
       }
     }
@@ -786,8 +794,8 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
       if (pp < np) {
 #pragma unroll
         for (int j = 0; j < kPerThread; j++) {
-          const int c = t + kCombineThreads * j;
-          if (c >= kChunks) continue;
+          const int c = c0 + t + NT * j;
+          if (c >= c0 + kChunksW) continue;
           const int hq = PAIR ? 4 * ((c & 63) >> 4) : 4 * ((2 * (c & 31)) >> 4);
           const bf16x8 x = __builtin_bit_cast(bf16x8, v[pp][j]);
 #pragma unroll
@@ -803,8 +811,8 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
   // stage the merged 16 x D block as bf16 rows, then store each row with 16-byte writes
 #pragma unroll
   for (int j = 0; j < kPerThread; j++) {
-    const int c = t + kCombineThreads * j;
-    if (c >= kChunks) continue;
+    const int c = c0 + t + NT * j;
+    if (c >= c0 + kChunksW) continue;
     if constexpr (PAIR) {
       const int ln = c & 63, col = (c >> 6) * 32 + (ln & 15), hq = 4 * (ln >> 4);
 #pragma unroll
@@ -825,9 +833,9 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
   // The output is not read again by this call, so it is stored nontemporally (streamed past the
   // caches): decode calls 0.7-2 % and FP8 decode calls 1.6 % faster. Marking the partial loads
   // the same way made ragged decode calls 5 % slower.
-  constexpr int kRowChunks = D / 8;  // 16-byte chunks per output row
-  for (int c = t; c < 16 * kRowChunks; c += kCombineThreads) {
-    const int r = c / kRowChunks, k = c % kRowChunks;
+  constexpr int kRowChunks = D / 8 / DS;  // 16-byte chunks per output row (this workgroup's columns)
+  for (int c = t; c < 16 * kRowChunks; c += NT) {
+    const int r = c / kRowChunks, k = ds * kRowChunks + c % kRowChunks;
     const int h = hb * 16 + r;
     if (h < H)
       __builtin_nontemporal_store(*(const u32x4*)(&stage[r * kOutStride + 8 * k]),
@@ -892,8 +900,17 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
     if (e != hipSuccess) return e;
   }
   if (nsplit == 1 || !(phases & 2)) return hipSuccess;
-  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB>), dim3((unsigned)(ntok * HB)), dim3(kCombineThreads), 0, stream, ws_o, ws_ml,
-                     sink, (__bf16*)out, (int)H, nsplit, nxcc);
+  // column split of the merge: more workgroups when there are few (token, head block) pairs
+  const int64_t pairs = ntok * HB;
+  if constexpr (D == 512) {
+    if (pairs <= 320) {
+      hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB, 4>), dim3((unsigned)(pairs * 4)), dim3(kCombineThreads / 4),
+                         0, stream, ws_o, ws_ml, sink, (__bf16*)out, (int)H, nsplit, nxcc);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB, 1>), dim3((unsigned)pairs), dim3(kCombineThreads), 0, stream,
+                     ws_o, ws_ml, sink, (__bf16*)out, (int)H, nsplit, nxcc);
   return hipGetLastError();
 }
 
