@@ -206,7 +206,8 @@ def main():
         ws_bytes = sa.sparse_attn_workspace_bytes(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)
         ws = sa.new_workspace(ws_bytes, dev)
 
-        nsplit = sa.sparse_attn_num_splits(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)
+        nsplit = (sa.sparse_attn_fp8_num_splits(cfg.B, cfg.S, cfg.H, cfg.K) if fp8 else
+                  sa.sparse_attn_num_splits(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K))
 
         attn = sa.sparse_attn_fp8 if fp8 else sa.sparse_attn
 
@@ -220,7 +221,9 @@ def main():
             x = sets[i % nsets]
             split_phase(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], x["scale"], out=out, workspace=ws)
 
-        hb = 1 if cfg.H <= 16 else (2 if cfg.H <= 32 else (4 if cfg.H <= 64 else 8))
+        groups = sa.sparse_attn_head_groups(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K, fp8)
+        hg = cfg.H // groups  # heads per (token, head group)
+        hb = 1 if hg <= 16 else (2 if hg <= 32 else (4 if hg <= 64 else 8))
         kernel_name = f"sparse_attn_kernel<{cfg.D},{hb},fp8>" if fp8 else f"sparse_attn_kernel<{cfg.D},{hb}>"
         work = [sparse_work(x, nsplit, 584 if fp8 else None) for x in sets]
         units_per_step = cfg.B * cfg.S
@@ -229,7 +232,7 @@ def main():
         workload = (f"{args.config} sparse_attn{'_fp8 (584-byte MODEL1 rows)' if fp8 else ''} B={cfg.B} S={cfg.S} "
                     f"H={cfg.H} D={cfg.D} T={cfg.T} K={cfg.K}, {nsets} rotating input sets")
         extra_cfg = {"B": cfg.B, "S": cfg.S, "H": cfg.H, "D": cfg.D, "T": cfg.T, "K": cfg.K,
-                     "num_splits": sa.sparse_attn_num_splits(cfg.B, cfg.S, cfg.H, cfg.D, cfg.K)}
+                     "head_groups": groups, "num_splits": nsplit}
 
         ntok = cfg.B * cfg.S
         toks = np.arange(ntok) if args.config != "prefill" else np.arange(0, ntok, 64)

@@ -75,13 +75,32 @@ size_t sparse_attn_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, i
 /*
  * The split count sparse_attn_fwd uses for num_splits = 0 (each token's K
  * slots are cut into this many contiguous ranges processed by separate
- * workgroups and merged afterwards). It depends on B*S and K only: never more
- * than 256 workgroups (one per CU) in all, at most K's 32-slot tile count and
- * 16, and within that the count that balances each workgroup's tile loop
- * against the partials written and merged (a cost fitted to measured decode
- * calls). Returns 1 for invalid sizes.
+ * workgroups and merged afterwards), per token and head group (see
+ * sparse_attn_head_groups: the count applies to the B*S*groups pairs). It
+ * never gives more than 256 workgroups (one per CU) in all, at most K's
+ * 32-slot tile count and 16, and within that the count that balances each
+ * workgroup's tile loop against the partials written and merged (a cost
+ * fitted to measured decode calls). Returns 1 for invalid sizes.
  */
 int sparse_attn_num_splits(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K);
+
+/*
+ * The number of head groups sparse_attn_fwd (fp8 = 0) or sparse_attn_fp8_fwd
+ * (fp8 = 1) cuts each token's heads into: 1, or 2 (groups of H / 2 heads, each
+ * processed by its own workgroups like a token of H / 2 heads) at D = 512 with
+ * 64 or more heads (a multiple of 32) when B*S <= 32, and for bf16 rows also
+ * when two groups keep at least 2 splits and as many workgroups as one. The
+ * split count of sparse_attn_num_splits is per token and head group. Returns 1
+ * for invalid sizes. Pure host function (no HIP call).
+ */
+int sparse_attn_head_groups(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K, int fp8);
+
+/*
+ * The split count sparse_attn_fp8_fwd uses for num_splits = 0 (D = 512; per
+ * token and head group, as sparse_attn_num_splits for bf16 rows). Returns 1
+ * for invalid sizes.
+ */
+int sparse_attn_fp8_num_splits(int64_t B, int64_t S, int64_t H, int64_t K);
 
 /*
  * q          device, bf16 [B][S][H][D]

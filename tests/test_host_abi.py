@@ -91,10 +91,23 @@ def test_noalloc_rejects_oversize_before_any_hip_call():
 
 
 def test_workspace_policy():
-    assert sa.sparse_attn_num_splits(64, 1, 128, 512, 1152) == 4
-    # the library's split counts at measured decode shapes (each within 3 % of the fastest)
-    for ntok, want in ((8, 9), (16, 8), (24, 7), (32, 6), (40, 6), (48, 5), (80, 3), (96, 2), (128, 2), (192, 1)):
+    # bf16 rows, 128 heads at D = 512: two head groups of 64 at <= 32 tokens and at 40, 56 and 64 tokens
+    # (where they keep >= 2 splits and as many workgroups), so the split count is per (token, head
+    # group); one group at 48 and from 72 tokens on
+    for ntok, want in ((4, 9), (8, 8), (16, 6), (24, 5), (32, 4), (40, 3), (48, 5), (56, 2), (64, 2), (72, 3),
+                       (80, 3), (96, 2), (128, 2), (192, 1)):
         assert sa.sparse_attn_num_splits(ntok, 1, 128, 512, 1152) == want, ntok
+    # no head groups below 64 heads or at D = 64: the split count is the token's own
+    assert sa.sparse_attn_num_splits(8, 1, 32, 512, 1152) == 9
+    assert sa.sparse_attn_num_splits(8, 1, 128, 64, 1152) == 9
+    for ntok, g16, g8 in ((8, 2, 2), (32, 2, 2), (40, 2, 1), (48, 1, 1), (56, 2, 1), (64, 2, 1), (72, 1, 1), (4096, 1, 1)):
+        assert sa.sparse_attn_head_groups(ntok, 1, 128, 512, 1152) == g16, ntok
+        assert sa.sparse_attn_head_groups(ntok, 1, 128, 512, 1152, fp8=True) == g8, ntok
+    assert sa.sparse_attn_head_groups(8, 1, 96, 512, 1152) == 2 and sa.sparse_attn_head_groups(8, 1, 48, 512, 1152) == 1
+    assert sa.sparse_attn_head_groups(8, 1, 100, 512, 1152) == 1  # not a multiple of 32
+    # FP8 rows keep one group at 64 tokens: 4 splits, and the workspace query covers both row formats
+    assert sa.sparse_attn_fp8_num_splits(64, 1, 128, 1152) == 4
+    assert sa.sparse_attn_workspace_bytes(64, 1, 128, 512, 1152) == 64 * 4 * 128 * (512 * 2 + 8)
     # never more than one workgroup per CU (256) in all, never more than the tiles or 16
     for ntok in range(1, 300):
         for K in (1, 32, 100, 512, 1152, 2048, 65536):

@@ -21,6 +21,8 @@ from .api import (  # noqa: F401
     sparse_attn_merge,
     sparse_attn_noalloc,
     sparse_attn_split,
+    sparse_attn_fp8_num_splits,
+    sparse_attn_head_groups,
     sparse_attn_num_splits,
     sparse_attn_workspace_bytes,
     topk_bitmask_build,

@@ -21,7 +21,8 @@ _lock = threading.Lock()
 SA_STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_ALIGN", 4: "SA_ERR_UNSUPPORTED",
              5: "SA_ERR_WORKSPACE", 6: "SA_ERR_HIP"}
 
-EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_fwd",
+EXPORTED = ["sa_status_string", "sparse_attn_workspace_bytes", "sparse_attn_num_splits", "sparse_attn_head_groups",
+            "sparse_attn_fp8_num_splits", "sparse_attn_fwd",
             "sparse_attn_fwd_noalloc",
             "sparse_attn_split_fwd", "sparse_attn_merge_fwd", "sparse_attn_fp8_fwd", "sparse_attn_fp8_split_fwd",
             "sparse_attn_fp8_merge_fwd", "topk_bitmask_shape", "topk_bitmask_build",
@@ -54,6 +55,10 @@ def _load():
         lib.sparse_attn_workspace_bytes.restype = ctypes.c_size_t
         lib.sparse_attn_num_splits.argtypes = [I64, I64, I64, I64, I64]
         lib.sparse_attn_num_splits.restype = I
+        lib.sparse_attn_head_groups.argtypes = [I64, I64, I64, I64, I64, I]
+        lib.sparse_attn_head_groups.restype = I
+        lib.sparse_attn_fp8_num_splits.argtypes = [I64, I64, I64, I64]
+        lib.sparse_attn_fp8_num_splits.restype = I
         for name in ("sparse_attn_fwd", "sparse_attn_split_fwd", "sparse_attn_merge_fwd"):
             getattr(lib, name).argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I, P, ctypes.c_size_t, P]
             getattr(lib, name).restype = I
@@ -127,6 +132,14 @@ _ws_cache: dict = {}
 
 def sparse_attn_num_splits(B: int, S: int, H: int, D: int, K: int) -> int:
     return int(_load().sparse_attn_num_splits(B, S, H, D, K))
+
+
+def sparse_attn_head_groups(B: int, S: int, H: int, D: int, K: int, fp8: bool = False) -> int:
+    return int(_load().sparse_attn_head_groups(B, S, H, D, K, int(bool(fp8))))
+
+
+def sparse_attn_fp8_num_splits(B: int, S: int, H: int, K: int) -> int:
+    return int(_load().sparse_attn_fp8_num_splits(B, S, H, K))
 
 
 def sparse_attn_workspace_bytes(B: int, S: int, H: int, D: int, K: int, num_splits: int = 0) -> int:

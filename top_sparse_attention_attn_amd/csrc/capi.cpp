@@ -10,7 +10,7 @@
 extern "C" {
 int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
                               int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K, float scale,
-                              int nsplit, void* ws, int phases, int fp8, void* stream);
+                              int nsplit, void* ws, int phases, int fp8, int G, void* stream);
 int sa_internal_head_blocks(int64_t H);
 size_t sa_internal_sparse_ws_bytes(int64_t ntok, int64_t H, int64_t D, int nsplit);
 size_t sa_internal_scratch_bytes(void);
@@ -72,9 +72,37 @@ int choose_splits(int64_t B, int64_t S, int64_t K, int requested) {
   return (int)n;
 }
 
-size_t sparse_ws_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int nsplit) {
+// Head groups: each token's H heads may be cut into G = 2 groups of H / 2, each processed like a
+// token of its own (twice the workgroups, each with half the heads: half the query load and half the
+// per-tile chain; a gathered row is then copied by both groups' workgroups). At D = 512 with 64 or
+// more heads (a multiple of 32): with at most 32 tokens always (decode calls 10-19 % faster at 4-16
+// tokens, 2-12 % at 24-32, FP8 rows 2-19 %), and for bf16 rows beyond that when two groups still get
+// at least 2 splits and at least as many workgroups as one group (40 tokens 8 %, 64 tokens 2.4-3.5 %
+// faster; 48 tokens, with fewer workgroups, 3 % slower, and 96, with one split, 14 % slower). FP8 rows
+// beyond 32 tokens keep one group: each group expands every row it copies (48 and 64 tokens 15-28 %
+// slower).
+int head_groups(int64_t ntok, int64_t H, int64_t D, int64_t K, int fp8) {
+  if (D != 512 || H < 64 || H % 32 != 0 || ntok <= 0) return 1;
+  if (ntok <= 32) return 2;
+  if (fp8) return 1;
+  const int n1 = choose_splits(ntok, 1, K, 0), n2 = choose_splits(2 * ntok, 1, K, 0);
+  return (n2 >= 2 && 2 * n2 >= n1) ? 2 : 1;
+}
+
+size_t sparse_ws_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int G, int nsplit) {
   if (nsplit <= 1) return 0;
-  return sa_internal_sparse_ws_bytes(B * S, H, D, nsplit);
+  return sa_internal_sparse_ws_bytes(B * S * G, H / G, D, nsplit);
+}
+
+// Workspace for a call of this shape, bf16 or FP8 rows alike (the larger of the two).
+size_t sparse_ws_bytes_any(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K, int num_splits) {
+  size_t need = 0;
+  for (int fp8 = 0; fp8 < 2; fp8++) {
+    const int G = head_groups(B * S, H, D, K, fp8);
+    const size_t w = sparse_ws_bytes(B, S, H, D, G, choose_splits(B * G, S, K, num_splits));
+    if (w > need) need = w;
+  }
+  return need;
 }
 
 // noalloc: take the workspace from the library's scratch array instead of the arguments
@@ -92,9 +120,10 @@ static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink
   if (!q || !attn_sink || !out || (K > 0 && !topk_idxs) || (T > 0 && K > 0 && !kv)) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || (!fp8 && kv && !aligned16(kv))) return SA_ERR_ALIGN;
   if (((uintptr_t)attn_sink & 3u) || (topk_idxs && ((uintptr_t)topk_idxs & 3u))) return SA_ERR_ALIGN;
-  const int nsplit = choose_splits(B, S, K, num_splits);
-  if (B * S * nsplit > ((int64_t)1 << 31) - 1) return SA_ERR_SHAPE;  // (token, split) pairs are int
-  const size_t need = sparse_ws_bytes(B, S, H, D, nsplit);
+  const int G = head_groups(B * S, H, D, K, fp8);
+  const int nsplit = choose_splits(B * G, S, K, num_splits);
+  if (B * S * G * nsplit > ((int64_t)1 << 31) - 1) return SA_ERR_SHAPE;  // (token, split) pairs are int
+  const size_t need = sparse_ws_bytes(B, S, H, D, G, nsplit);
   if (noalloc) {
     if (need > sa_internal_scratch_bytes()) return SA_ERR_WORKSPACE;
     workspace = nullptr;
@@ -104,7 +133,7 @@ static int sparse_attn_run(const void* q, const void* kv, const float* attn_sink
     if ((uintptr_t)workspace & 255u) return SA_ERR_ALIGN;
   }
   const int rc = sa_internal_launch_sparse(q, kv, attn_sink, topk_idxs, out, B, S, H, D, T, K, scale, nsplit,
-                                           need > 0 ? workspace : nullptr, phases, fp8, stream);
+                                           need > 0 ? workspace : nullptr, phases, fp8, G, stream);
   return rc == 0 ? SA_OK : SA_ERR_HIP;
 }
 
@@ -144,15 +173,25 @@ const char* sa_status_string(int status) {
   }
 }
 
+int sparse_attn_head_groups(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K, int fp8) {
+  if (!sparse_sizes_ok(B, S, H, D, K)) return 1;
+  return head_groups(B * S, H, D, K, fp8 != 0);
+}
+
+int sparse_attn_fp8_num_splits(int64_t B, int64_t S, int64_t H, int64_t K) {
+  if (!sparse_sizes_ok(B, S, H, 512, K)) return 1;
+  return choose_splits(B * head_groups(B * S, H, 512, K, 1), S, K, 0);
+}
+
 int sparse_attn_num_splits(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K) {
   if (!sparse_sizes_ok(B, S, H, D, K)) return 1;
-  return choose_splits(B, S, K, 0);
+  return choose_splits(B * head_groups(B * S, H, D, K, 0), S, K, 0);
 }
 
 size_t sparse_attn_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int64_t K, int num_splits) {
   if (!sparse_sizes_ok(B, S, H, D, K) || num_splits < 0) return 0;
   if (H < 1 || H > 128) return 0;
-  return sparse_ws_bytes(B, S, H, D, choose_splits(B, S, K, num_splits));
+  return sparse_ws_bytes_any(B, S, H, D, K, num_splits);
 }
 
 int sparse_attn_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* out,

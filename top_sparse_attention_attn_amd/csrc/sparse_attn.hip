@@ -134,7 +134,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
                                           const float* __restrict__ sink, const int* __restrict__ idx,
                                           __bf16* __restrict__ out, __bf16* __restrict__ ws_o,
                                           float* __restrict__ ws_ml, int S, int H, int T, int K, int nsplit,
-                                          int nxcc, int tok_mul, float scale_log2) {
+                                          int ngrp, int nxcc, int tok_mul, float scale_log2) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
   constexpr int NB = SCORE ? 0 : G::kDBV;  // output column blocks of this wave
@@ -160,12 +160,15 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
   // tokens have fewer causally valid slots) and the rounds do not load queries and store outputs
   // all at the same time.
   if (nsplit == 1) pair = (int)(((long)pair * tok_mul) % (long)gridDim.x);
+  // tok is a (token, head group) pair: token rtok's heads hg*H .. hg*H+H-1 (H is the group's head
+  // count), so the q and out rows of tok sit at (tok * H + h) * D as for a token of H heads
   const int tok = pair / nsplit, split = pair % nsplit;
-  const int b = tok / S;
+  const int rtok = tok / ngrp, hg = tok - rtok * ngrp;
+  const int b = rtok / S;
   const int ntiles_all = (K + kTile - 1) / kTile;
   const int t0 = (int)(((long)split * ntiles_all) / nsplit);
   const int ntl = (int)(((long)(split + 1) * ntiles_all) / nsplit) - t0;
-  const int* __restrict__ idx_tok = idx + (size_t)tok * K;
+  const int* __restrict__ idx_tok = idx + (size_t)rtok * K;
   const __bf16* __restrict__ kv_b = (const __bf16*)kv + (size_t)(F8 ? 0 : b) * T * D;
   static_assert(!F8 || D == 512, "FP8 rows hold D = 512");
   u32x4 kv8rs = {};  // FP8: the batch's rows as a buffer resource
@@ -582,7 +585,7 @@ __device__ __forceinline__ void run_split(Smem<D, HB>& sm, const __bf16* __restr
       float f = 0.f;
       if (nsplit == 1) {
         if (h < H) {
-          const float sk = sink[h];
+          const float sk = sink[hg * H + h];
           if (__builtin_isnan(sk)) {
             f = __builtin_nanf("");
           } else if (sk == __builtin_huge_valf()) {
@@ -685,13 +688,13 @@ template <int D, int HB, bool F8, bool NT>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ sink,
     const int* __restrict__ idx, __bf16* __restrict__ out, __bf16* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int S, int H, int T, int K, int nsplit, int nxcc, int tok_mul, float scale_log2) {
+    int S, int H, int T, int K, int nsplit, int G, int nxcc, int tok_mul, float scale_log2) {
   __shared__ __attribute__((aligned(16))) Smem<D, HB> sm;
   if (threadIdx.x < 256)  // waves 0-3
-    run_split<D, HB, true, F8, NT>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, nxcc, tok_mul,
+    run_split<D, HB, true, F8, NT>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, G, nxcc, tok_mul,
                                scale_log2);
   else
-    run_split<D, HB, false, F8, NT>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, nxcc, tok_mul,
+    run_split<D, HB, false, F8, NT>(sm, q, kv, sink, idx, out, ws_o, ws_ml, S, H, T, K, nsplit, G, nxcc, tok_mul,
                                 scale_log2);
 }
 
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
                                                                    const float* __restrict__ ws_ml,
                                                                    const float* __restrict__ sink,
                                                                    __bf16* __restrict__ out, int H, int nsplit,
-                                                                   int nxcc) {
+                                                                   int ngrp, int nxcc) {
   using G = Geo<D>;
   constexpr int HP = HB * 16;
   constexpr int NT = kCombineThreads / DS;             // threads of this workgroup
@@ -743,7 +746,7 @@ __global__ __launch_bounds__(kCombineThreads) void sparse_attn_combine_kernel(co
   float sk = kNegInf;
   if (t < 16) {
     const int h = hb * 16 + t;
-    sk = h < H ? sink[h] : kNegInf;
+    sk = h < H ? sink[(tok % ngrp) * H + h] : kNegInf;  // head group tok % ngrp of its token
 #pragma unroll
     for (int p = 0; p < kMaxSplits; p++) {
       const float2 v = p < nsplit ? *(const float2*)(ws_ml + (((size_t)tok * nsplit + p) * HP + h) * 2)
@@ -883,8 +886,10 @@ static int token_multiplier(int64_t n) {
 template <int D, int HB, bool F8>
 static hipError_t launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx, void* out,
                                 int64_t B, int64_t S, int64_t H, int64_t T, int64_t K, float scale, int nsplit,
-                                void* ws, int phases, hipStream_t stream) {
-  const int64_t ntok = B * S;
+                                void* ws, int phases, int G, hipStream_t stream) {
+  // G head groups: each token is G (token, head group) pairs of H / G heads, all of them "tokens" below
+  const int64_t ntok = B * S * G;
+  H /= G;
   const int64_t n = ntok * nsplit;
   const WsLayout L = ws_layout(ntok, HB, D, nsplit);
   __bf16* ws_o = nsplit > 1 ? (__bf16*)ws : nullptr;
@@ -894,8 +899,8 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
     // one token per batch: the gathered rows are streamed (see run_split)
     auto kern = S == 1 ? sparse_attn_kernel<D, HB, F8, true> : sparse_attn_kernel<D, HB, F8, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(kThreads), 0, stream, (const __bf16*)q, kv, sink, idx,
-                       (__bf16*)out, ws_o, ws_ml, (int)S, (int)H, (int)T, (int)K, nsplit, nxcc, token_multiplier(n),
-                       scale * kLog2e);
+                       (__bf16*)out, ws_o, ws_ml, (int)S, (int)H, (int)T, (int)K, nsplit, G, nxcc,
+                       token_multiplier(n), scale * kLog2e);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -905,12 +910,12 @@ static hipError_t launch_sparse(const void* q, const void* kv, const float* sink
   if constexpr (D == 512) {
     if (pairs <= 320) {
       hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB, 4>), dim3((unsigned)(pairs * 4)), dim3(kCombineThreads / 4),
-                         0, stream, ws_o, ws_ml, sink, (__bf16*)out, (int)H, nsplit, nxcc);
+                         0, stream, ws_o, ws_ml, sink, (__bf16*)out, (int)H, nsplit, G, nxcc);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((sparse_attn_combine_kernel<D, HB, 1>), dim3((unsigned)pairs), dim3(kCombineThreads), 0, stream,
-                     ws_o, ws_ml, sink, (__bf16*)out, (int)H, nsplit, nxcc);
+                     ws_o, ws_ml, sink, (__bf16*)out, (int)H, nsplit, G, nxcc);
   return hipGetLastError();
 }
 
@@ -926,14 +931,16 @@ extern "C" int sa_internal_head_blocks(int64_t H) {
 // fp8: kv holds FP8 rows of 584 bytes (D = 512)
 extern "C" int sa_internal_launch_sparse(const void* q, const void* kv, const float* sink, const int32_t* idx,
                                          void* out, int64_t B, int64_t S, int64_t H, int64_t D, int64_t T, int64_t K,
-                                         float scale, int nsplit, void* ws, int phases, int fp8, void* stream) {
+                                         float scale, int nsplit, void* ws, int phases, int fp8, int G,
+                                         void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  const int hb = sa_internal_head_blocks(H);
+  if (G < 1 || H % G != 0) return 1;
+  const int hb = sa_internal_head_blocks(H / G);
   hipError_t e;
 #define SA_CASE(DD, HBB) \
-  e = sa::launch_sparse<DD, HBB, false>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, phases, st)
+  e = sa::launch_sparse<DD, HBB, false>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, phases, G, st)
 #define SA_CASE8(HBB) \
-  e = sa::launch_sparse<512, HBB, true>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, phases, st)
+  e = sa::launch_sparse<512, HBB, true>(q, kv, sink, idx, out, B, S, H, T, K, scale, nsplit, ws, phases, G, st)
   if (fp8) {
     if (D != 512) return 2;
     if (hb == 1) SA_CASE8(1); else if (hb == 2) SA_CASE8(2); else if (hb == 4) SA_CASE8(4); else SA_CASE8(8);
