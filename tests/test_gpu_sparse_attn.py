@@ -413,7 +413,7 @@ def test_split_merge_special_cases():
     assert torch.isnan(out[:, :, 1]).all()
 
 
-@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("splits", [1, 2, 4])
 def test_split_then_merge_equals_one_call(splits):
     """The two phases called apart give exactly the one-call result."""
     inp = _custom(16, 1, 128, 512, 600, 512, seed=51)

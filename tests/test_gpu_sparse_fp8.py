@@ -39,7 +39,7 @@ def test_fp8_vs_oracle(oracle_impl, H):
     assert_close(to64(out).reshape(ref.shape), ref, f"fp8 H={H}")
 
 
-@pytest.mark.parametrize("num_splits", [1, 4])
+@pytest.mark.parametrize("num_splits", [1, 2, 4])
 def test_fp8_equals_bf16_kernel_on_dequantized_rows(oracle_impl, num_splits):
     """The FP8 path expands rows to bf16 before the unchanged score/softmax/PV code, so on the
     same (exactly representable) rows it must give the bf16 kernel's output bit for bit."""
@@ -92,7 +92,7 @@ def test_fp8_decode_config_sampled(oracle_impl):
     assert_close(to64(out[toks]).reshape(ref.shape), ref, "fp8 decode")
 
 
-@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("splits", [1, 2, 4])
 def test_fp8_split_then_merge_equals_one_call(splits):
     """sparse_attn_fp8_split_fwd then sparse_attn_fp8_merge_fwd give exactly the one-call result."""
     B, S, H, T, K = 16, 1, 128, 600, 512
