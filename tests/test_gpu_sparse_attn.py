@@ -127,6 +127,22 @@ def test_padded_head_blocks(oracle_impl, H, S, splits):
     assert_close(to64(out).reshape(ref.shape), ref, f"H={H} S={S} splits={splits}")
 
 
+@pytest.mark.parametrize("H", [96, 64])
+@pytest.mark.parametrize("S,splits", [(1, 0), (1, 2), (2, 1), (2, 3)])
+def test_head_groups_with_padded_blocks(oracle_impl, H, S, splits):
+    """Two head groups: 96 heads are groups of 48 in a 64-head block (the padded heads are never
+    written), 64 heads groups of 32; each group's queries, sink entries and output rows are those
+    of its own heads."""
+    B = 4
+    assert sa.sparse_attn_head_groups(B, S, H, 512, 300) == 2
+    inp = _custom(B, S, H, 512, 400, 300, seed=130 + H + S + splits)
+    out = torch.full_like(inp["q"], 5.0)
+    _run(inp, out=out, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = sparse_reference(oracle_impl, inp["q"], inp["kv"], inp["attn_sink"], inp["topk_idxs"], inp["scale"])
+    assert_close(to64(out).reshape(ref.shape), ref, f"H={H} S={S} splits={splits}")
+
+
 @pytest.mark.parametrize("K", [0, 1, 31, 33])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_few_slots(oracle_impl, K, splits):

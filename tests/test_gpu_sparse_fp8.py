@@ -52,6 +52,22 @@ def test_fp8_equals_bf16_kernel_on_dequantized_rows(oracle_impl, num_splits):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("H,num_splits", [(96, 0), (96, 2), (64, 3)])
+def test_fp8_head_groups_with_padded_blocks(oracle_impl, H, num_splits):
+    """Two head groups (96 heads: 48 per group in a padded 64-head block; 64: 32 per group): bit
+    for bit the bf16 kernel's output on the dequantised rows, and within tolerance of the oracle."""
+    B, S, T, K = 4, 1, 700, 500
+    assert sa.sparse_attn_head_groups(B, S, H, 512, K, fp8=True) == 2
+    q, kv8, sink, idx = _case(B, S, H, T, K, seed=17 + H)
+    deq = torch.from_numpy(oracle_impl.fp8_dequant(kv8.numpy())).to(torch.bfloat16)
+    a = _run(q, kv8, sink, idx, 512 ** -0.5, num_splits=num_splits)
+    b = sa.sparse_attn(q.to(DEV), deq.to(DEV), sink.to(DEV), idx.to(DEV), 512 ** -0.5, num_splits=num_splits)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = oracle_impl.sparse_attn_fp8(bits(q), kv8.numpy(), sink.numpy(), idx.numpy(), 512 ** -0.5)
+    assert_close(to64(a).reshape(ref.shape), ref, f"fp8 H={H} splits={num_splits}")
+
+
 def test_fp8_single_row_is_the_dequantized_row(oracle_impl):
     """One valid slot and sink -inf: each head's output is that row, dequantized (exactly, for
     these scale bytes) and rounded to bf16."""
